@@ -1,0 +1,275 @@
+"""Pins of the fp64 oracle against facts outside itself: the OCP MX format
+tables, closed forms, brute force on tiny inputs and invariants the pages
+state (chunk-union prefill equals the per-token path; a layer's result does
+not depend on how tokens are batched or ordered)."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_matches_ocp_table():
+    rows = _read_table("ocp_mx_e2m1.txt")
+    assert len(rows) == 16
+    for bits, val in rows:
+        code = int(bits, 2)
+        got = oracle.e2m1_value(code)
+        assert got == float(val)
+        assert math.copysign(1.0, got) == math.copysign(1.0, float(val))  # -0 for code 8
+    assert np.array_equal(oracle.E2M1_VALUES, [float(v) for _, v in rows])
+
+
+def test_e8m0_matches_ocp_table():
+    for hx, val in _read_table("ocp_mx_e8m0.txt"):
+        got = oracle.e8m0_value(int(hx, 16))
+        if val == "NaN":
+            assert math.isnan(got)
+        else:
+            assert got == 2.0 ** int(val[2:])
+    for b in range(254):
+        assert oracle.e8m0_value(b + 1) == 2.0 * oracle.e8m0_value(b)
+
+
+def test_dequant_exhaustive_exact_in_fp32():
+    # every (code, scale byte) pair once: row b uses scale byte b, codes 0..15
+    q = np.zeros((256, 16), dtype=np.uint8)           # K = 32 per row
+    q[:, :8] = np.array([c | ((c + 8) << 4) for c in range(8)], dtype=np.uint8)
+    s = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    w = oracle.dequant(q, s)
+    table = {int(b, 2): float(v) for b, v in _read_table("ocp_mx_e2m1.txt")}
+    for b in range(256):
+        for c in range(16):
+            pos = 2 * c if c < 8 else 2 * (c - 8) + 1
+            got = w[b, pos]
+            if b == 255:
+                assert math.isnan(got)
+                continue
+            want = table[c] * 2.0 ** (b - 127)
+            assert got == want
+            # exactly representable in fp32 wherever fp32 has the range
+            # (|value| < 2^128; 6 * 2^127 overflows)
+            if abs(got) < 2.0 ** 128:
+                assert float(np.float32(got)) == got
+
+
+def test_dequant_layout_by_hand():
+    # one row, K = 64 (two blocks). Byte 0 = 0x21: element 0 is code 1 (0.5),
+    # element 1 is code 2 (1.0). Byte 1 = 0xF7: element 2 = code 7 (6.0),
+    # element 3 = code 15 (-6.0). Byte 16 = 0x5B: element 32 = code 11 (-1.5),
+    # element 33 = code 5 (3.0). Scales: block 0 = 0x80 (x2), block 1 = 0x7E (x0.5).
+    q = np.zeros((1, 32), dtype=np.uint8)
+    q[0, 0], q[0, 1], q[0, 16] = 0x21, 0xF7, 0x5B
+    s = np.array([[0x80, 0x7E]], dtype=np.uint8)
+    w = oracle.dequant(q, s)
+    want = np.zeros(64)
+    want[0], want[1], want[2], want[3] = 1.0, 2.0, 12.0, -12.0
+    want[32], want[33] = -0.75, 1.5
+    assert np.array_equal(w[0], want)
+
+
+# ---------------------------------------------------------------- router
+
+def test_router_logits_match_exact_sums():
+    rng = np.random.default_rng(0)
+    T, E, d = 3, 5, 96
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    wr = (0.02 * rng.standard_normal((E, d))).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    got = oracle.router_logits(x, wr)
+    gotb = oracle.router_logits(x, wr, bias)
+    for t in range(T):
+        for e in range(E):
+            exact = math.fsum(float(xf[t, i]) * float(wr[e, i]) for i in range(d))
+            assert got[t, e] == np.float32(exact)
+            assert gotb[t, e] == np.float32(np.float32(exact) + bias[e])
+
+
+def _brute_topk(row, k):
+    E = len(row)
+    best, best_key = None, None
+    for sub in itertools.combinations(range(E), k):
+        key = (math.fsum(float(row[e]) for e in sub), tuple(-e for e in sub))
+        if best_key is None or key > best_key:
+            best, best_key = sub, key
+    return sorted(best, key=lambda e: (-float(row[e]), e))
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 3), (6, 1), (7, 7)])
+def test_topk_brute_force_subsets(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    for trial in range(60):
+        if trial % 3 == 0:  # many exact ties
+            row = rng.integers(-2, 3, E).astype(np.float32)
+        else:
+            row = rng.standard_normal(E).astype(np.float32)
+        idx, gate = oracle.topk_gates(row[None, :], k)
+        assert list(idx[0]) == _brute_topk(row, k)
+
+
+def test_topk_special_cases():
+    E, k = 8, 3
+    idx, gate = oracle.topk_gates(np.zeros((1, E), np.float32), k)
+    assert list(idx[0]) == [0, 1, 2]
+    assert np.allclose(gate[0], 1.0 / k, rtol=0, atol=1e-15)
+    # k = 1: gate exactly one
+    row = np.random.default_rng(1).standard_normal((4, E)).astype(np.float32)
+    _, g1 = oracle.topk_gates(row, 1)
+    assert np.all(g1 == 1.0)
+    # k = E: full softmax in logit order
+    idx, g = oracle.topk_gates(row, E)
+    for t in range(4):
+        sm = softmax(row[t].astype(np.float64))
+        assert np.allclose(g[t], sm[idx[t]], rtol=1e-14, atol=0)
+        assert list(idx[t]) == list(np.lexsort((np.arange(E), -row[t])))
+
+
+def test_gates_sum_to_one_and_bias_selects():
+    cfg = synth.CONFIGS[1]
+    E, k = cfg.E, cfg.k
+    bias = synth.skew_bias(4, E)
+    x0 = np.zeros((1, cfg.d), dtype=np.uint16)
+    logits = oracle.router_logits(x0, synth.gen_router_w(cfg), bias)
+    assert np.array_equal(logits[0], bias)  # x = 0: logits are the bias
+    idx, gate = oracle.topk_gates(logits, k)
+    assert list(idx[0]) == list(np.argsort(-bias.astype(np.float64), kind="stable")[:k])
+    assert np.allclose(gate[0], softmax(bias[idx[0]].astype(np.float64)), rtol=1e-14)
+    x = synth.gen_x(cfg, T=64)
+    _, g = oracle.topk_gates(oracle.router_logits(x, synth.gen_router_w(cfg)), k)
+    assert np.all(np.abs(g.sum(axis=1) - 1.0) < 1e-12)
+    assert np.all(np.abs(g.astype(np.float32).sum(axis=1, dtype=np.float32) - 1.0) < 1e-6)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def test_silu_closed_form():
+    z = np.concatenate([np.linspace(-40, 40, 2001), [0.0, 1e-300, -1e-300]])
+    assert np.allclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    big = oracle.silu(np.array([-1000.0, 1000.0, -750.0]))
+    assert not np.any(np.isnan(big))
+    assert big[0] == 0.0 and big[1] == 1000.0 and big[2] == 0.0
+
+
+def _selection_matrix(rows, cols, pick, code, scale_bytes):
+    """MXFP4 matrix with one non-zero per row: W[r, pick[r]] = E2M1[code] *
+    2^(scale_bytes[r] - 127); every other element is code 0."""
+    q = np.zeros((rows, cols // 2), dtype=np.uint8)
+    s = np.full((rows, cols // 32), 127, dtype=np.uint8)
+    for r in range(rows):
+        c = pick[r]
+        q[r, c // 2] |= (code << 4) if c % 2 else code
+        s[r, c // 32] = scale_bytes[r]
+    return q, s
+
+
+def test_expert_ffn_selection_closed_form():
+    rng = np.random.default_rng(7)
+    d, f = 64, 96
+    pg = rng.integers(0, d, f)
+    pu = rng.integers(0, d, f)
+    pd = rng.integers(0, f, d)
+    sg = rng.integers(124, 131, f)
+    su = rng.integers(124, 131, f)
+    sd = rng.integers(124, 131, d)
+    w = {}
+    w["gate_q"], w["gate_s"] = _selection_matrix(f, d, pg, 5, sg)    # code 5 = 3.0
+    w["up_q"], w["up_s"] = _selection_matrix(f, d, pu, 10, su)       # code 10 = -1.0
+    w["down_q"], w["down_s"] = _selection_matrix(d, f, pd, 4, sd)    # code 4 = 2.0
+    x = rng.standard_normal((3, d))
+    o, h = oracle.expert_ffn(x, w, return_h=True)
+    g = 3.0 * x[:, pg] * 2.0 ** (sg - 127)
+    u = -1.0 * x[:, pu] * 2.0 ** (su - 127)
+    want_h = g * expit(g) * u
+    want_o = 2.0 * want_h[:, pd] * 2.0 ** (sd - 127)
+    assert np.allclose(h, want_h, rtol=1e-14, atol=0)
+    assert np.allclose(o, want_o, rtol=1e-14, atol=0)
+
+
+def test_zero_weights_give_zero():
+    cfg = synth.CONFIGS[0]
+    W = synth.gen_weights(cfg)
+    for code_byte in (0x00, 0x88):  # +0 and -0 codes
+        Z = dict(W)
+        for name in ("gate_q", "up_q", "down_q"):
+            Z[name] = np.full_like(W[name], code_byte)
+        x = synth.gen_x(cfg, T=2)
+        r = oracle.layer_forward(x, synth.gen_router_w(cfg), None, synth.ExpertSource(cfg, Z), cfg.k)
+        assert np.all(r["y64"] == 0.0)
+
+
+def test_scale_homogeneity():
+    cfg = synth.CONFIGS[0]
+    W = synth.gen_weights(cfg)
+    x = synth.gen_x(cfg, T=2)
+    wr = synth.gen_router_w(cfg)
+    base = oracle.layer_forward(x, wr, None, synth.ExpertSource(cfg, W), cfg.k)["y64"]
+    for name in ("down_s", "up_s"):
+        W2 = dict(W)
+        W2[name] = (W[name] + 1).astype(np.uint8)
+        y2 = oracle.layer_forward(x, wr, None, synth.ExpertSource(cfg, W2), cfg.k)["y64"]
+        assert np.array_equal(y2, 2.0 * base)
+
+
+# ---------------------------------------------------------------- whole layer
+
+@pytest.mark.parametrize("ci,T", [(0, 1), (0, 5), (1, 3)])
+def test_dense_masked_equals_sparse(ci, T):
+    cfg = synth.CONFIGS[ci]
+    W = synth.gen_weights(cfg)
+    src = synth.ExpertSource(cfg, W)
+    x = synth.gen_x(cfg, T=T)
+    wr = synth.gen_router_w(cfg)
+    sparse = oracle.layer_forward(x, wr, None, src, cfg.k)["y64"]
+    dense = oracle.dense_masked_forward(x, wr, None, src, cfg.k, cfg.E)
+    rms = np.sqrt(np.mean(sparse ** 2))
+    assert np.max(np.abs(dense - sparse)) <= 1e-12 * rms
+
+
+def test_batch_and_permutation_invariance():
+    cfg = synth.CONFIGS[1]
+    W = synth.gen_weights(cfg)
+    src = synth.ExpertSource(cfg, W)
+    x = synth.gen_x(cfg, T=6)
+    wr = synth.gen_router_w(cfg)
+    full = oracle.layer_forward(x, wr, None, src, cfg.k)
+    for t in range(6):
+        one = oracle.layer_forward(x[t:t + 1], wr, None, src, cfg.k)
+        assert np.array_equal(one["idx"][0], full["idx"][t])
+        assert np.array_equal(one["y64"][0], full["y64"][t])
+    p = np.array([3, 0, 5, 1, 4, 2])
+    perm = oracle.layer_forward(x[p], wr, None, src, cfg.k)
+    assert np.array_equal(perm["y64"], full["y64"][p])
+    assert np.array_equal(perm["idx"], full["idx"][p])
+
+
+# ---------------------------------------------------------------- grouping
+
+@pytest.mark.parametrize("T,k,E", [(1, 2, 8), (37, 4, 16), (300, 16, 896), (5, 8, 8)])
+def test_group_pairs_matches_stable_sort(T, k, E):
+    rng = np.random.default_rng(T + k + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm = oracle.group_pairs(idx, E)
+    flat = idx.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(perm, np.argsort(flat, kind="stable"))
