@@ -1,0 +1,176 @@
+/*
+ * k3moe.h - C ABI of the MI355X (gfx950) forward pass of one sparse
+ * Mixture-of-Experts layer whose expert weights are stored in MXFP4.
+ *
+ * The layer is the MoE block of the Kimi K3 model that the kimi-k3-in-c pages
+ * describe: a router picks the top 16 of 896 routed experts per token
+ * (CHANGELOG walk-through, 0.1.0 section: "MoE router, top-16 of 896"), each
+ * expert is a gated-linear (SwiGLU) FFN (same section, printed "SiTU-GLU"),
+ * and expert weights are 4-bit E2M1 codes with a shared E8M0 scale per 32
+ * elements, consumed as packed nibbles (same section: "MXFP4 matmul consumes
+ * packed nibbles directly"; "four reductions" overview: experts are already
+ * nibbles, about half a byte per parameter). Tokens routed to the same expert
+ * are grouped so each expert's weights are read once per call (CHANGELOG
+ * walk-through, Unreleased section: chunk-union prefill, identical output to
+ * the per-token path).
+ *
+ * What one forward computes, per token t (x[t] is bf16, everything else fp32):
+ *   l[e]   = sum_i x[t,i] * Wr[e,i]  (+ bias[e])                  router logits
+ *   S      = the k experts with the largest l, ties to the lower index,
+ *            ordered by (l descending, index ascending)
+ *   gate_j = exp(l_j - l_max) / sum_{i in S} exp(l_i - l_max)     renormalised
+ *   for j in S:  g = Wg_j x, u = Wu_j x, h = SiLU(g) * u,  o_j = Wd_j h
+ *   y[t]   = sum_j gate_j * o_j
+ * with SiLU(z) = z / (1 + e^-z). The pages leave the router function, tie
+ * rule and normalisation open; the readings above are the plainest ones.
+ *
+ * Conventions shared by every entry point
+ * - Pointers are DEVICE pointers on the handle's device unless marked HOST.
+ * - Every argument is checked before anything is enqueued; a failed check
+ *   returns K3MOE_EINVAL (or K3MOE_EUNSUPPORTED) and writes nothing. The
+ *   library never aborts, exits or prints (the pages' engine rejects bad
+ *   input loudly instead of defaulting: CHANGELOG walk-through, config
+ *   reader that refuses unknown configs).
+ * - Work is enqueued on the caller's HIP stream (NULL = the legacy default
+ *   stream) in stream order, with no host synchronisation. Faults inside
+ *   kernels surface at the caller's next synchronisation.
+ * - A handle owns one workspace; calls on one handle must not overlap (use one
+ *   handle per concurrent stream).
+ * - T = 0 is valid and does nothing.
+ * - NaN/Inf inputs propagate and are not checked; a NaN router logit never
+ *   wins a selection (it ranks as -inf), so selected indices stay in range.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define K3MOE_OK             0
+#define K3MOE_EINVAL        -1   /* bad argument: null pointer, bad size, misalignment */
+#define K3MOE_ENOMEM        -2   /* device memory for the workspace is not available */
+#define K3MOE_EHIP          -3   /* a HIP runtime call or kernel launch failed */
+#define K3MOE_EUNSUPPORTED  -4   /* valid but outside what this build supports */
+
+typedef struct k3moe k3moe;  /* opaque handle */
+
+/* Layer shape (HOST struct, copied by k3moe_create).
+ * Supported: d % 128 == 0 and 128 <= d <= 16384; f % 128 == 0 and
+ * 128 <= f <= 16384; 1 <= k <= E <= 4096; k <= 64; 1 <= max_tokens and
+ * max_tokens * k < 2^31. Anything else returns K3MOE_EINVAL (malformed) or
+ * K3MOE_EUNSUPPORTED (well-formed but beyond these limits). */
+typedef struct {
+  int32_t d_model;     /* d: hidden size */
+  int32_t n_experts;   /* E: routed experts */
+  int32_t top_k;       /* k: experts per token */
+  int32_t d_ff;        /* f: expert FFN width */
+  int32_t max_tokens;  /* largest T any later call may pass; sizes the workspace */
+  uint32_t flags;      /* reserved, must be 0 */
+} k3moe_config;
+
+/* Layer weights (HOST struct of DEVICE pointers). BORROWED: they must stay
+ * valid and unchanged until k3moe_destroy; the library never writes or
+ * frees them. Every pointer must be 16-byte aligned.
+ *
+ * MXFP4 layout (OCP Microscaling v1.0, E2M1 elements + E8M0 block scales):
+ * a matrix is [rows][K] with K the reduction dimension, stored as
+ *   codes  [rows][K/2]  uint8: element 2i in the low nibble, 2i+1 in the high
+ *   scales [rows][K/32] uint8: E8M0 byte b means 2^(b-127); 0xFF is NaN
+ * and the experts of one tensor are stacked: expert e starts at
+ * e * rows * K/2 (codes) and e * rows * K/32 (scales). */
+typedef struct {
+  const float*   router_w;  /* [E][d] fp32, row-major */
+  const float*   router_b;  /* [E] fp32 added to every token's logits, or NULL */
+  const uint8_t* gate_q;    /* [E][f][d/2]  gate projection codes (rows = f, K = d) */
+  const uint8_t* gate_s;    /* [E][f][d/32] gate projection scales */
+  const uint8_t* up_q;      /* [E][f][d/2]  up projection codes */
+  const uint8_t* up_s;      /* [E][f][d/32] */
+  const uint8_t* down_q;    /* [E][d][f/2]  down projection codes (rows = d, K = f) */
+  const uint8_t* down_s;    /* [E][d][f/32] */
+} k3moe_weights;
+
+/* Create a handle on HIP device `device`: validates cfg and w, checks free
+ * device memory before allocating (refusing before allocating, as the pages'
+ * engine does for an over-budget KV cache), allocates the workspace for
+ * cfg->max_tokens tokens and derives the router weight split used by the
+ * prefill router. On success *out receives the handle and K3MOE_OK is
+ * returned; on any failure *out is set to NULL (when out is not NULL),
+ * nothing stays allocated and an error code is returned. Synchronous. */
+int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device,
+                 k3moe** out);
+
+/* Destroy a handle: synchronises the handle's device (so none of its kernels
+ * is still running), frees the workspace and the handle. NULL-safe. Never
+ * frees weights. */
+void k3moe_destroy(k3moe* h);
+
+/* Static text for a status code. Never NULL. */
+const char* k3moe_status_str(int status);
+
+/* Bytes of device workspace a handle with this config allocates, or a
+ * negative status if cfg is invalid. HOST-only, no device call. */
+int64_t k3moe_workspace_bytes(const k3moe_config* cfg);
+
+/* The whole layer: router -> top-k -> grouping -> experts -> combine.
+ *   x         [T][d] bf16 activations, 16-byte aligned
+ *   T         0 <= T <= max_tokens
+ *   y         [T][d] fp32 output, 16-byte aligned; fully overwritten
+ *   topk_idx  [T][k] int32 selected experts in selection order, or NULL
+ *   topk_gate [T][k] fp32 gates matching topk_idx, or NULL
+ *   stream    hipStream_t, or NULL for the default stream
+ * y must not alias x, the weights or the index/gate outputs. */
+int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y,
+                        int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* Router step alone: fp32 logits, top-k selection with ties to the lower
+ * index, and gates renormalised over the selection.
+ *   logits [T][E] fp32 output, or NULL to skip writing them
+ *   idx    [T][k] int32 output; gate [T][k] fp32 output (both required) */
+int k3moe_route(k3moe* h, const void* x, int32_t T, float* logits,
+                int32_t* idx, float* gate, void* stream);
+
+/* Grouping step alone (the chunk-union step: each routed expert's tokens are
+ * gathered so its weights are read once). Input idx [T][k] int32 with every
+ * value in [0, E) and the k values of one token distinct (values outside
+ * [0, E) are counted nowhere and make the outputs undefined; they never
+ * cause out-of-bounds writes). Outputs:
+ *   counts  [E]    pairs routed to each expert
+ *   offsets [E+1]  exclusive prefix sum of counts (offsets[E] = T*k)
+ *   perm    [T*k]  pair ids p = t*k + j ordered by (expert, t, j)  */
+int k3moe_group(k3moe* h, const int32_t* idx, int32_t T, int32_t* counts,
+                int32_t* offsets, int32_t* perm, void* stream);
+
+/* Expert step alone with the caller's routing: grouping, the expert FFNs and
+ * the gate-weighted combine. idx/gate [T][k] as produced by k3moe_route
+ * (same constraints as k3moe_group; any gate values are accepted). */
+int k3moe_experts_forward(k3moe* h, const void* x, int32_t T,
+                          const int32_t* idx, const float* gate, float* y,
+                          void* stream);
+
+/* Stage timing, a profiling aid. Between k3moe_profile_begin and
+ * k3moe_profile_end every forward records a HIP event before and after each
+ * stage's kernel launch(es) on the call's own stream, for at most max_calls
+ * launches per stage (later launches run untimed). k3moe_profile_end waits
+ * for the recorded events and writes, per stage, the summed milliseconds and
+ * the number of timed launches into HOST arrays of K3MOE_NUM_STAGES entries,
+ * then releases the events. The stages: */
+#define K3MOE_STAGE_ROUTER_LOGITS 0  /* router logits (one kernel) */
+#define K3MOE_STAGE_TOPK          1  /* top-k + gates (one kernel) */
+#define K3MOE_STAGE_GROUP         2  /* histogram, scan, permute (three kernels) */
+#define K3MOE_STAGE_QUANT_X       3  /* activation split for the MFMA path (one kernel) */
+#define K3MOE_STAGE_GATEUP        4  /* gate/up projection + SwiGLU (one kernel) */
+#define K3MOE_STAGE_CLEAR_Y       5  /* output clear before scatter-add (one kernel) */
+#define K3MOE_STAGE_DOWN          6  /* down projection + combine (one kernel) */
+#define K3MOE_NUM_STAGES          7
+int k3moe_profile_begin(k3moe* h, int32_t max_calls);
+int k3moe_profile_end(k3moe* h, float* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3MOE_H */

@@ -1,0 +1,190 @@
+"""ctypes binding of libk3moe.so with the C entry points' names.
+
+Tensors are torch tensors on the handle's GPU; only their data pointers and
+the current HIP stream handle cross the boundary.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libk3moe.so")
+
+K3MOE_OK = 0
+K3MOE_EINVAL = -1
+K3MOE_ENOMEM = -2
+K3MOE_EHIP = -3
+K3MOE_EUNSUPPORTED = -4
+
+
+class K3MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {k3moe_status_str(status)} (status {status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("router_w", "router_b", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    d_model: int
+    n_experts: int
+    top_k: int
+    d_ff: int
+    max_tokens: int
+    flags: int = 0
+
+    def _c(self) -> _Config:
+        return _Config(self.d_model, self.n_experts, self.top_k, self.d_ff, self.max_tokens,
+                       self.flags)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libk3moe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with mxfp4_expert_matmul_amd/build.py "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.k3moe_status_str.argtypes = [ctypes.c_int]
+    lib.k3moe_status_str.restype = ctypes.c_char_p
+    lib.k3moe_workspace_bytes.argtypes = [ctypes.POINTER(_Config)]
+    lib.k3moe_workspace_bytes.restype = i64
+    lib.k3moe_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), ctypes.c_int,
+                                 ctypes.POINTER(vp)]
+    lib.k3moe_create.restype = ctypes.c_int
+    lib.k3moe_destroy.argtypes = [vp]
+    lib.k3moe_destroy.restype = None
+    lib.k3moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_layer_forward.restype = ctypes.c_int
+    lib.k3moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_route.restype = ctypes.c_int
+    lib.k3moe_group.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_group.restype = ctypes.c_int
+    lib.k3moe_experts_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_experts_forward.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != K3MOE_OK:
+        raise K3MoEError(rc, where)
+
+
+def k3moe_status_str(status: int) -> str:
+    return load_library().k3moe_status_str(int(status)).decode()
+
+
+def k3moe_workspace_bytes(cfg: Config) -> int:
+    c = cfg._c()
+    return int(load_library().k3moe_workspace_bytes(ctypes.byref(c)))
+
+
+def k3moe_create(cfg: Config, weights: dict, device: int = 0) -> ctypes.c_void_p:
+    """weights: dict of device tensors router_w, router_b (or None), gate_q,
+    gate_s, up_q, up_s, down_q, down_s in the layout of include/k3moe.h."""
+    lib = load_library()
+    c = cfg._c()
+    w = _Weights(*[weights.get(n).data_ptr() if weights.get(n) is not None else None
+                   for n, _ in _Weights._fields_])
+    out = ctypes.c_void_p()
+    rc = lib.k3moe_create(ctypes.byref(c), ctypes.byref(w), int(device), ctypes.byref(out))
+    _check(rc, "k3moe_create")
+    return out
+
+
+def k3moe_destroy(handle) -> None:
+    if handle:
+        load_library().k3moe_destroy(handle)
+
+
+def k3moe_layer_forward(handle, x, y, topk_idx=None, topk_gate=None, stream=None, device=None):
+    T = x.shape[0]
+    rc = load_library().k3moe_layer_forward(handle, _ptr(x), T, _ptr(y), _ptr(topk_idx),
+                                            _ptr(topk_gate), _stream(stream, device or x.device))
+    _check(rc, "k3moe_layer_forward")
+
+
+def k3moe_route(handle, x, idx, gate, logits=None, stream=None):
+    rc = load_library().k3moe_route(handle, _ptr(x), x.shape[0], _ptr(logits), _ptr(idx),
+                                    _ptr(gate), _stream(stream, x.device))
+    _check(rc, "k3moe_route")
+
+
+def k3moe_group(handle, idx, counts, offsets, perm, stream=None):
+    rc = load_library().k3moe_group(handle, _ptr(idx), idx.shape[0], _ptr(counts), _ptr(offsets),
+                                    _ptr(perm), _stream(stream, idx.device))
+    _check(rc, "k3moe_group")
+
+
+def k3moe_experts_forward(handle, x, idx, gate, y, stream=None):
+    rc = load_library().k3moe_experts_forward(handle, _ptr(x), x.shape[0], _ptr(idx), _ptr(gate),
+                                              _ptr(y), _stream(stream, x.device))
+    _check(rc, "k3moe_experts_forward")
+
+
+class Layer:
+    """Owns one k3moe handle. Weights are borrowed: keep the tensors alive."""
+
+    def __init__(self, cfg: Config, weights: dict, device: int = 0):
+        self.cfg = cfg
+        self.device = device
+        self._weights = weights  # keep borrowed tensors alive
+        self.handle = k3moe_create(cfg, weights, device)
+
+    def forward(self, x, stream=None):
+        """x: [T][d] bf16 (torch.bfloat16 or int16 bit patterns) on the GPU.
+        Returns (y fp32 [T][d], idx int32 [T][k], gate fp32 [T][k])."""
+        import torch
+        T = x.shape[0]
+        dev = x.device
+        y = torch.empty((T, self.cfg.d_model), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, self.cfg.top_k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, self.cfg.top_k), dtype=torch.float32, device=dev)
+        k3moe_layer_forward(self.handle, x, y, idx, gate, stream=stream)
+        return y, idx, gate
+
+    def close(self):
+        if self.handle:
+            k3moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

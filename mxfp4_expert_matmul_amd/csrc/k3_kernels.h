@@ -1,0 +1,57 @@
+// Host-side launchers of the k3moe kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns the launch status; callers
+// have validated all sizes and pointers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace k3 {
+
+// Prefill grouped GEMM tile: tokens (sorted pairs) per tile.
+constexpr int kTileM = 64;
+// Pairs per block of the grouping step.
+constexpr int kGroupChunk = 256;
+// Largest T served by the GEMV (decode) expert path.
+constexpr int kGemvMaxT = 4;
+// Largest T served by the GEMV router.
+constexpr int kRouterGemvMaxT = 8;
+
+struct Shape {
+  int d, E, k, f;
+};
+
+struct ExpertWeights {
+  const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+};
+
+// router_topk.hip
+hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const float* wr,
+                                const float* bias, float* logits, hipStream_t st);
+hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,
+                       hipStream_t st);
+
+// group.hip
+hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* bhist, int32_t* tiles,
+                        int32_t* ntiles, hipStream_t st);
+
+// gemv.hip (decode path, T <= kGemvMaxT)
+hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
+                              const int32_t* idx, float* h32, hipStream_t st);
+hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
+                            const float* gate, const float* h32, float* y, hipStream_t st);
+
+// gemm.hip (prefill path)
+hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,
+                          hipStream_t st);
+hipError_t launch_clear_y(float* y, int T, int d, hipStream_t st);
+hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, const uint8_t* xq,
+                              const uint8_t* xs, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* tiles, const int32_t* ntiles, int max_tiles,
+                              uint8_t* hq, uint8_t* hs, hipStream_t st);
+hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const float* gate,
+                            const int32_t* offsets, const int32_t* perm, const int32_t* tiles,
+                            const int32_t* ntiles, int max_tiles, const uint8_t* hq,
+                            const uint8_t* hs, float* y, hipStream_t st);
+
+}  // namespace k3

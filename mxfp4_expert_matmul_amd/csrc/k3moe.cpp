@@ -1,0 +1,419 @@
+// Host side of the k3moe C ABI: argument checks, workspace planning and
+// allocation, and dispatch of the router, grouping and expert kernels.
+// The library never aborts, exits or prints; every failure is a status code.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "k3_kernels.h"
+#include "k3moe.h"
+
+using k3::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Byte offsets of every workspace buffer for one config.
+struct Plan {
+  size_t logits, idx, gate, counts, offsets, perm, bhist, tiles, ntiles, xq, xs, hq, hs, h32;
+  size_t total;
+  int max_tiles;
+};
+
+int check_config(const k3moe_config* c) {
+  if (!c) return K3MOE_EINVAL;
+  if (c->flags != 0u) return K3MOE_EINVAL;
+  if (c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 ||
+      c->max_tokens <= 0)
+    return K3MOE_EINVAL;
+  if (c->top_k > c->n_experts) return K3MOE_EINVAL;
+  if (c->d_model % 32 != 0 || c->d_ff % 32 != 0) return K3MOE_EINVAL;  // whole MX blocks
+  if (c->d_model % 128 != 0 || c->d_ff % 128 != 0) return K3MOE_EUNSUPPORTED;
+  if (c->d_model > 8192 || c->d_ff > 4096) return K3MOE_EUNSUPPORTED;
+  if (c->n_experts > 4096 || c->top_k > 64) return K3MOE_EUNSUPPORTED;
+  if ((int64_t)c->max_tokens * c->top_k >= (int64_t)1 << 31) return K3MOE_EUNSUPPORTED;
+  return K3MOE_OK;
+}
+
+Plan make_plan(const k3moe_config* c) {
+  const size_t T = (size_t)c->max_tokens, E = (size_t)c->n_experts, k = (size_t)c->top_k;
+  const size_t d = (size_t)c->d_model, f = (size_t)c->d_ff;
+  const size_t P = T * k;
+  const size_t NB = (P + k3::kGroupChunk - 1) / k3::kGroupChunk;
+  const size_t tiles = (P + k3::kTileM - 1) / k3::kTileM + std::min(E, P);
+  const size_t tg = std::min(T, (size_t)k3::kGemvMaxT);
+  Plan p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.logits = take(T * E * 4);
+  p.idx = take(P * 4);
+  p.gate = take(P * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.perm = take(P * 4);
+  p.bhist = take(NB * E * 4);
+  p.tiles = take(tiles * 2 * 4);
+  p.ntiles = take(4);
+  p.xq = take(2 * T * d);
+  p.xs = take(2 * T * (d / 32));
+  p.hq = take(2 * P * f);
+  p.hs = take(2 * P * (f / 32));
+  p.h32 = take(tg * k * f * 4);
+  p.total = o;
+  p.max_tiles = (int)tiles;
+  return p;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~DeviceGuard() {
+    if (ok && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct k3moe {
+  k3moe_config cfg;
+  k3moe_weights w;
+  int device;
+  Plan plan;
+  uint8_t* ws;
+  // typed views into ws
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* bhist;
+  int32_t* tiles;
+  int32_t* ntiles;
+  uint8_t* xq;
+  uint8_t* xs;
+  uint8_t* hq;
+  uint8_t* hs;
+  float* h32;
+  // stage timing (k3moe_profile_begin / k3moe_profile_end)
+  bool prof_on;
+  int prof_cap;
+  int prof_n[K3MOE_NUM_STAGES];
+  std::vector<hipEvent_t> prof_ev[K3MOE_NUM_STAGES];  // 2 per recorded launch
+};
+
+namespace {
+
+void profile_release(k3moe* h) {
+  for (int i = 0; i < K3MOE_NUM_STAGES; ++i) {
+    for (hipEvent_t ev : h->prof_ev[i]) (void)hipEventDestroy(ev);
+    h->prof_ev[i].clear();
+    h->prof_n[i] = 0;
+  }
+  h->prof_on = false;
+  h->prof_cap = 0;
+}
+
+Shape shape_of(const k3moe* h) {
+  return Shape{h->cfg.d_model, h->cfg.n_experts, h->cfg.top_k, h->cfg.d_ff};
+}
+
+k3::ExpertWeights experts_of(const k3moe* h) {
+  return k3::ExpertWeights{h->w.gate_q, h->w.gate_s, h->w.up_q, h->w.up_s, h->w.down_q, h->w.down_s};
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? K3MOE_OK : K3MOE_EHIP; }
+
+// Runs one stage's launch, bracketed by HIP events on the same stream when
+// stage timing is on.
+template <class F>
+hipError_t stage(k3moe* h, int id, hipStream_t st, F&& launch) {
+  const bool rec = h->prof_on && h->prof_n[id] < h->prof_cap;
+  if (rec) {
+    hipError_t e = hipEventRecord(h->prof_ev[id][2 * h->prof_n[id]], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (rec) {
+    e = hipEventRecord(h->prof_ev[id][2 * h->prof_n[id] + 1], st);
+    if (e != hipSuccess) return e;
+    h->prof_n[id]++;
+  }
+  return hipSuccess;
+}
+
+int run_router(k3moe* h, const uint16_t* x, int T, float* logits, int32_t* idx, float* gate,
+               hipStream_t st) {
+  const Shape s = shape_of(h);
+  hipError_t e = stage(h, K3MOE_STAGE_ROUTER_LOGITS, st, [&] {
+    return k3::launch_router_logits(x, T, s, h->w.router_w, h->w.router_b, logits, st);
+  });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  e = stage(h, K3MOE_STAGE_TOPK, st, [&] { return k3::launch_topk(logits, T, s, idx, gate, st); });
+  return hip_status(e);
+}
+
+int run_experts(k3moe* h, const uint16_t* x, int T, const int32_t* idx, const float* gate,
+                float* y, hipStream_t st) {
+  const Shape s = shape_of(h);
+  const k3::ExpertWeights w = experts_of(h);
+  hipError_t e;
+  if (T <= k3::kGemvMaxT) {
+    e = stage(h, K3MOE_STAGE_GATEUP, st,
+              [&] { return k3::launch_gemv_gateup(x, T, s, w, idx, h->h32, st); });
+    if (e != hipSuccess) return K3MOE_EHIP;
+    e = stage(h, K3MOE_STAGE_DOWN, st,
+              [&] { return k3::launch_gemv_down(T, s, w, idx, gate, h->h32, y, st); });
+    return hip_status(e);
+  }
+  e = stage(h, K3MOE_STAGE_GROUP, st, [&] {
+    return k3::launch_group(idx, T, s, h->counts, h->offsets, h->perm, h->bhist, h->tiles,
+                            h->ntiles, st);
+  });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  e = stage(h, K3MOE_STAGE_QUANT_X, st,
+            [&] { return k3::launch_quant_x(x, T, s.d, h->xq, h->xs, st); });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  // the tile bound for this call's T (never above the workspace's)
+  const size_t P = (size_t)T * s.k;
+  const int max_tiles = (int)((P + k3::kTileM - 1) / k3::kTileM + std::min((size_t)s.E, P));
+  e = stage(h, K3MOE_STAGE_GATEUP, st, [&] {
+    return k3::launch_gemm_gateup(T, s, w, h->xq, h->xs, h->offsets, h->perm, h->tiles,
+                                  h->ntiles, max_tiles, h->hq, h->hs, st);
+  });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  e = stage(h, K3MOE_STAGE_CLEAR_Y, st, [&] { return k3::launch_clear_y(y, T, s.d, st); });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  e = stage(h, K3MOE_STAGE_DOWN, st, [&] {
+    return k3::launch_gemm_down(T, s, w, gate, h->offsets, h->perm, h->tiles, h->ntiles,
+                                max_tiles, h->hq, h->hs, y, st);
+  });
+  return hip_status(e);
+}
+
+int check_tokens(const k3moe* h, int32_t T) {
+  if (!h) return K3MOE_EINVAL;
+  if (T < 0 || T > h->cfg.max_tokens) return K3MOE_EINVAL;
+  return K3MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* k3moe_status_str(int status) {
+  switch (status) {
+    case K3MOE_OK: return "ok";
+    case K3MOE_EINVAL: return "invalid argument";
+    case K3MOE_ENOMEM: return "not enough device memory for the workspace";
+    case K3MOE_EHIP: return "HIP runtime or kernel launch failure";
+    case K3MOE_EUNSUPPORTED: return "configuration not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int64_t k3moe_workspace_bytes(const k3moe_config* cfg) {
+  int rc = check_config(cfg);
+  if (rc != K3MOE_OK) return rc;
+  return (int64_t)make_plan(cfg).total;
+}
+
+int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3moe** out) {
+  if (out) *out = nullptr;
+  if (!out || !w) return K3MOE_EINVAL;
+  int rc = check_config(cfg);
+  if (rc != K3MOE_OK) return rc;
+  const void* req[] = {w->router_w, w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const void* p : req)
+    if (!p || !aligned(p, 16)) return K3MOE_EINVAL;
+  if (w->router_b && !aligned(w->router_b, 16)) return K3MOE_EINVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return K3MOE_EHIP;
+  if (device < 0 || device >= ndev) return K3MOE_EINVAL;
+  DeviceGuard guard(device);
+  if (!guard.ok) return K3MOE_EHIP;
+  const Plan plan = make_plan(cfg);
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_EHIP;
+  if (plan.total > free_b) return K3MOE_ENOMEM;  // refuse before allocating
+  k3moe* h = new (std::nothrow) k3moe();
+  if (!h) return K3MOE_ENOMEM;
+  h->cfg = *cfg;
+  h->w = *w;
+  h->device = device;
+  h->plan = plan;
+  void* base = nullptr;
+  if (hipMalloc(&base, plan.total) != hipSuccess || !base) {
+    (void)hipGetLastError();  // clear the sticky allocation error
+    delete h;
+    return K3MOE_ENOMEM;
+  }
+  h->ws = static_cast<uint8_t*>(base);
+  h->logits = reinterpret_cast<float*>(h->ws + plan.logits);
+  h->idx = reinterpret_cast<int32_t*>(h->ws + plan.idx);
+  h->gate = reinterpret_cast<float*>(h->ws + plan.gate);
+  h->counts = reinterpret_cast<int32_t*>(h->ws + plan.counts);
+  h->offsets = reinterpret_cast<int32_t*>(h->ws + plan.offsets);
+  h->perm = reinterpret_cast<int32_t*>(h->ws + plan.perm);
+  h->bhist = reinterpret_cast<int32_t*>(h->ws + plan.bhist);
+  h->tiles = reinterpret_cast<int32_t*>(h->ws + plan.tiles);
+  h->ntiles = reinterpret_cast<int32_t*>(h->ws + plan.ntiles);
+  h->xq = h->ws + plan.xq;
+  h->xs = h->ws + plan.xs;
+  h->hq = h->ws + plan.hq;
+  h->hs = h->ws + plan.hs;
+  h->h32 = reinterpret_cast<float*>(h->ws + plan.h32);
+  *out = h;
+  return K3MOE_OK;
+}
+
+void k3moe_destroy(k3moe* h) {
+  if (!h) return;
+  {
+    DeviceGuard guard(h->device);
+    if (guard.ok) {
+      (void)hipDeviceSynchronize();
+      profile_release(h);
+      (void)hipFree(h->ws);
+    }
+  }
+  delete h;
+}
+
+int k3moe_route(k3moe* h, const void* x, int32_t T, float* logits, int32_t* idx, float* gate,
+                void* stream) {
+  int rc = check_tokens(h, T);
+  if (rc != K3MOE_OK) return rc;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !idx || !gate || !aligned(x, 16) || !aligned(idx, 4) || !aligned(gate, 4))
+    return K3MOE_EINVAL;
+  if (logits && !aligned(logits, 4)) return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  float* lg = logits ? logits : h->logits;
+  return run_router(h, static_cast<const uint16_t*>(x), T, lg, idx, gate,
+                    static_cast<hipStream_t>(stream));
+}
+
+int k3moe_group(k3moe* h, const int32_t* idx, int32_t T, int32_t* counts, int32_t* offsets,
+                int32_t* perm, void* stream) {
+  int rc = check_tokens(h, T);
+  if (rc != K3MOE_OK) return rc;
+  if (!idx || !counts || !offsets || !perm) return K3MOE_EINVAL;
+  if (!aligned(idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4))
+    return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // T == 0 still writes zero counts and offsets
+  return hip_status(stage(h, K3MOE_STAGE_GROUP, st, [&] {
+    return k3::launch_group(idx, T, shape_of(h), counts, offsets, perm, h->bhist, h->tiles,
+                            h->ntiles, st);
+  }));
+}
+
+int k3moe_experts_forward(k3moe* h, const void* x, int32_t T, const int32_t* idx,
+                          const float* gate, float* y, void* stream) {
+  int rc = check_tokens(h, T);
+  if (rc != K3MOE_OK) return rc;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !idx || !gate || !y) return K3MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(idx, 4) || !aligned(gate, 4))
+    return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y,
+                     static_cast<hipStream_t>(stream));
+}
+
+int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y, int32_t* topk_idx,
+                        float* topk_gate, void* stream) {
+  int rc = check_tokens(h, T);
+  if (rc != K3MOE_OK) return rc;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return K3MOE_EINVAL;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_gate && !aligned(topk_gate, 4)))
+    return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : h->idx;
+  float* gate = topk_gate ? topk_gate : h->gate;
+  int rc2 = run_router(h, static_cast<const uint16_t*>(x), T, h->logits, idx, gate, st);
+  if (rc2 != K3MOE_OK) return rc2;
+  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y, st);
+}
+
+
+int k3moe_profile_begin(k3moe* h, int32_t max_calls) {
+  if (!h || max_calls <= 0 || max_calls > (1 << 20)) return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  profile_release(h);
+  for (int i = 0; i < K3MOE_NUM_STAGES; ++i) {
+    try {
+      h->prof_ev[i].resize(2 * (size_t)max_calls, nullptr);
+    } catch (...) {
+      profile_release(h);
+      return K3MOE_ENOMEM;
+    }
+    for (auto& ev : h->prof_ev[i]) {
+      if (hipEventCreate(&ev) != hipSuccess) {
+        ev = nullptr;
+        profile_release(h);
+        return K3MOE_EHIP;
+      }
+    }
+  }
+  h->prof_cap = max_calls;
+  h->prof_on = true;
+  return K3MOE_OK;
+}
+
+int k3moe_profile_end(k3moe* h, float* total_ms, int32_t* launches) {
+  if (!h || !total_ms || !launches) return K3MOE_EINVAL;
+  if (!h->prof_on) return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  int rc = K3MOE_OK;
+  for (int i = 0; i < K3MOE_NUM_STAGES; ++i) {
+    double sum = 0.0;
+    for (int n = 0; n < h->prof_n[i]; ++n) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(h->prof_ev[i][2 * n + 1]) != hipSuccess ||
+          hipEventElapsedTime(&ms, h->prof_ev[i][2 * n], h->prof_ev[i][2 * n + 1]) != hipSuccess) {
+        rc = K3MOE_EHIP;
+        continue;
+      }
+      sum += ms;
+    }
+    total_ms[i] = (float)sum;
+    launches[i] = h->prof_n[i];
+  }
+  profile_release(h);
+  return rc;
+}
+
+}  // extern "C"

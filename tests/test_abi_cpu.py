@@ -1,0 +1,72 @@
+"""The C-ABI library loads on a host without a GPU, exports every symbol
+include/k3moe.h declares, and rejects invalid configurations before any
+device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "k3moe.h")).read()
+    return sorted(set(re.findall(r"\b(k3moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mxfp4_expert_matmul_amd as k3m
+    if not os.path.exists(k3m.library_path()):
+        pytest.skip("libk3moe.so not built")
+    return k3m
+
+
+def test_exports_every_declared_symbol(lib):
+    dll = ctypes.CDLL(lib.library_path())
+    names = _declared()
+    assert {"k3moe_create", "k3moe_destroy", "k3moe_layer_forward", "k3moe_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(dll, n), n
+
+
+def test_status_strings(lib):
+    for code in (lib.K3MOE_OK, lib.K3MOE_EINVAL, lib.K3MOE_ENOMEM, lib.K3MOE_EHIP,
+                 lib.K3MOE_EUNSUPPORTED, 12345):
+        assert isinstance(lib.k3moe_status_str(code), str) and lib.k3moe_status_str(code)
+
+
+@pytest.mark.parametrize("cfg,want", [
+    ((128, 8, 2, 256, 1), "ok"),
+    ((7168, 896, 16, 2048, 4096), "ok"),
+    ((100, 8, 2, 256, 1), -1),       # d not whole MX blocks
+    ((160, 8, 2, 256, 1), -4),       # d % 128 != 0
+    ((128, 8, 9, 256, 1), -1),       # k > E
+    ((128, 8, 2, 256, 0), -1),       # no tokens
+    ((128, 8, 2, 8192, 1), -4),      # f beyond the supported range
+    ((128, 8000, 2, 256, 1), -4),    # E beyond the supported range
+    ((128, 8, 64, 256, 1), -1),      # k > E
+    ((128, 64, 64, 256, 2 ** 26), -4),  # T*k overflows int32
+])
+def test_workspace_bytes_validation(lib, cfg, want):
+    n = lib.k3moe_workspace_bytes(lib.Config(*cfg))
+    if want == "ok":
+        assert n > 0
+    else:
+        assert n == want
+
+
+def test_workspace_scales_with_tokens(lib):
+    a = lib.k3moe_workspace_bytes(lib.Config(7168, 896, 16, 2048, 1))
+    b = lib.k3moe_workspace_bytes(lib.Config(7168, 896, 16, 2048, 4096))
+    assert 0 < a < b < 600_000_000
+
+
+def test_create_without_gpu_returns_status(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host has a GPU")
+    with pytest.raises(lib.K3MoEError) as ei:
+        lib.Layer(lib.Config(128, 8, 2, 256, 1), {}, 0)
+    assert ei.value.status in (lib.K3MOE_EINVAL, lib.K3MOE_EHIP)
