@@ -136,8 +136,8 @@ int k3moe_route(k3moe* h, const void* x, int32_t T, float* logits,
 /* Grouping step alone (the chunk-union step: each routed expert's tokens are
  * gathered so its weights are read once). Input idx [T][k] int32 with every
  * value in [0, E) and the k values of one token distinct (values outside
- * [0, E) are counted nowhere and make the outputs undefined; they never
- * cause out-of-bounds writes). Outputs:
+ * [0, E) are dropped: counted nowhere, absent from perm). With T == 0, idx
+ * and perm may be NULL and counts/offsets are written as zeros. Outputs:
  *   counts  [E]    pairs routed to each expert
  *   offsets [E+1]  exclusive prefix sum of counts (offsets[E] = T*k)
  *   perm    [T*k]  pair ids p = t*k + j ordered by (expert, t, j)  */

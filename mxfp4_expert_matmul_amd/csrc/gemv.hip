@@ -92,39 +92,42 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   }
   const int n0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kGateUpRowsPerWave;
   const size_t qrow = (size_t)(d >> 1), srow = (size_t)nb;
+  // two row pairs per pass; all of a pass's loads are issued before any math
 #pragma unroll
-  for (int r = 0; r < kGateUpRowsPerWave; ++r) {
-    const int n = n0 + r;
-    if (n >= f) break;
-    const size_t row = (size_t)e * f + n;
-    const uint8_t* gqr = gq + row * qrow;
-    const uint8_t* uqr = uq + row * qrow;
-    const uint8_t* gsr = gs + row * srow;
-    const uint8_t* usr = us + row * srow;
-    uint4 qg[NBL], qu[NBL];
-    uint32_t sg[NBL], su[NBL];
+  for (int r0 = 0; r0 < kGateUpRowsPerWave; r0 += 2) {
+    uint4 qg[2][NBL], qu[2][NBL];
+    uint32_t sg[2][NBL], su[2][NBL];
 #pragma unroll
-    for (int b = 0; b < NBL; ++b) {
-      const int blk = lane + 64 * b;
-      if (blk < nb) {
-        qg[b] = *reinterpret_cast<const uint4*>(gqr + 16 * blk);
-        qu[b] = *reinterpret_cast<const uint4*>(uqr + 16 * blk);
-        sg[b] = gsr[blk];
-        su[b] = usr[blk];
+    for (int rr = 0; rr < 2; ++rr) {
+      const int n = min(n0 + r0 + rr, f - 1);
+      const size_t row = (size_t)e * f + n;
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) {
+        const int blk = lane + 64 * b;
+        if (blk < nb) {
+          qg[rr][b] = *reinterpret_cast<const uint4*>(gq + row * qrow + 16 * blk);
+          qu[rr][b] = *reinterpret_cast<const uint4*>(uq + row * qrow + 16 * blk);
+          sg[rr][b] = gs[row * srow + blk];
+          su[rr][b] = us[row * srow + blk];
+        }
       }
     }
-    float ga = 0.0f, ua = 0.0f;
 #pragma unroll
-    for (int b = 0; b < NBL; ++b) {
-      const int blk = lane + 64 * b;
-      if (blk < nb) {
-        ga = fmaf(block_dot_bf16(qg[b], xr[b]), e8m0_to_f32(sg[b]), ga);
-        ua = fmaf(block_dot_bf16(qu[b], xr[b]), e8m0_to_f32(su[b]), ua);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int n = n0 + r0 + rr;
+      float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NBL; ++b) {
+        const int blk = lane + 64 * b;
+        if (blk < nb) {
+          ga = fmaf(block_dot_bf16(qg[rr][b], xr[b]), e8m0_to_f32(sg[rr][b]), ga);
+          ua = fmaf(block_dot_bf16(qu[rr][b], xr[b]), e8m0_to_f32(su[rr][b]), ua);
+        }
       }
+      ga = wave_sum(ga);
+      ua = wave_sum(ua);
+      if (lane == 0 && n < f) h32[(size_t)pair * f + n] = silu_f32(ga) * ua;
     }
-    ga = wave_sum(ga);
-    ua = wave_sum(ua);
-    if (lane == 0) h32[(size_t)pair * f + n] = silu_f32(ga) * ua;
   }
 }
 
@@ -167,19 +170,27 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
         }
       }
     }
+    // all rows' loads first, then the math
+    uint4 q[kDownRowsPerBlock][NBF];
+    uint32_t sc[kDownRowsPerBlock][NBF];
 #pragma unroll
     for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      const int m = m0 + r;
-      if (m >= d) break;
-      const size_t row = (size_t)e * d + m;
+      const size_t row = (size_t)e * d + min(m0 + r, d - 1);
 #pragma unroll
       for (int b = 0; b < NBF; ++b) {
         const int blk = lane + 64 * b;
         if (blk < nbf) {
-          uint4 q = *reinterpret_cast<const uint4*>(dq + row * qrow + 16 * blk);
-          float sc = e8m0_to_f32(ds[row * srow + blk]);
-          acc[r] = fmaf(g * sc, block_dot_f32(q, hv[b]), acc[r]);
+          q[r][b] = *reinterpret_cast<const uint4*>(dq + row * qrow + 16 * blk);
+          sc[r][b] = ds[row * srow + blk];
         }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kDownRowsPerBlock; ++r) {
+#pragma unroll
+      for (int b = 0; b < NBF; ++b) {
+        const int blk = lane + 64 * b;
+        if (blk < nbf) acc[r] = fmaf(g * e8m0_to_f32(sc[r][b]), block_dot_f32(q[r][b], hv[b]), acc[r]);
       }
     }
   }
@@ -208,10 +219,10 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
   dim3 g1(T * s.k, (s.f + 4 * kGateUpRowsPerWave - 1) / (4 * kGateUpRowsPerWave));
 #define K3_GU(N) hipLaunchKernelGGL(gemv_gateup_kernel<N>, g1, dim3(256), 0, st, x, s.d, s.f, s.k, s.E, \
                                     w.gate_q, w.gate_s, w.up_q, w.up_s, idx, h32)
+  // d <= 8192: at most 4 blocks per lane
   if (nbl <= 1) K3_GU(1);
   else if (nbl <= 2) K3_GU(2);
-  else if (nbl <= 4) K3_GU(4);
-  else K3_GU(8);
+  else K3_GU(4);
 #undef K3_GU
   return hipGetLastError();
 }
@@ -223,9 +234,9 @@ hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const
   dim3 g2(T, (s.d + kDownRowsPerBlock - 1) / kDownRowsPerBlock);
 #define K3_DN(N) hipLaunchKernelGGL(gemv_down_kernel<N>, g2, dim3(256), 0, st, s.d, s.f, s.k, s.E, \
                                     w.down_q, w.down_s, idx, gate, h32, y)
+  // f <= 4096: at most 2 blocks per lane
   if (nbfl <= 1) K3_DN(1);
-  else if (nbfl <= 2) K3_DN(2);
-  else K3_DN(4);
+  else K3_DN(2);
 #undef K3_DN
   return hipGetLastError();
 }

@@ -321,7 +321,7 @@ int k3moe_group(k3moe* h, const int32_t* idx, int32_t T, int32_t* counts, int32_
                 int32_t* perm, void* stream) {
   int rc = check_tokens(h, T);
   if (rc != K3MOE_OK) return rc;
-  if (!idx || !counts || !offsets || !perm) return K3MOE_EINVAL;
+  if (!counts || !offsets || (T > 0 && (!idx || !perm))) return K3MOE_EINVAL;
   if (!aligned(idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(perm, 4))
     return K3MOE_EINVAL;
   DeviceGuard guard(h->device);

@@ -10,41 +10,56 @@
 namespace k3 {
 
 // ---------------------------------------------------------------- logits, small T
-// One wave per expert row; the row (d fp32) is streamed once with 16-byte
-// loads and applied to every token of the call. HBM-bound: E*d*4 bytes.
+// One workgroup (4 waves) per expert row: every thread loads its share of the
+// row (d/256 floats, all loads issued before use) and applies it to every
+// token of the call; partial sums meet in LDS. HBM-bound: E*d*4 bytes.
 template <int TMAX>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x, int T,
                                                           int d, const float* __restrict__ wr,
                                                           const float* __restrict__ bias, int E,
                                                           float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  __shared__ float part[4][TMAX];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
   const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * d);
+  constexpr int kMaxPer = 8;  // float4 per thread for d <= 8192
+  const int n4 = d >> 2;
+  float4 w[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n4) w[j] = row[i];
+  }
   float acc[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
-  const int n4 = d >> 2;
-  for (int i = lane; i < n4; i += 64) {
-    float4 w = row[i];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + 4 * i);
-        acc[t] = fmaf(bf16_bits_to_f32(xv.x & 0xffffu), w.x, acc[t]);
-        acc[t] = fmaf(bf16_bits_to_f32(xv.x >> 16), w.y, acc[t]);
-        acc[t] = fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w.z, acc[t]);
-        acc[t] = fmaf(bf16_bits_to_f32(xv.y >> 16), w.w, acc[t]);
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n4) {
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+          uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + 4 * i);
+          acc[t] = fmaf(bf16_bits_to_f32(xv.x & 0xffffu), w[j].x, acc[t]);
+          acc[t] = fmaf(bf16_bits_to_f32(xv.x >> 16), w[j].y, acc[t]);
+          acc[t] = fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w[j].z, acc[t]);
+          acc[t] = fmaf(bf16_bits_to_f32(xv.y >> 16), w[j].w, acc[t]);
+        }
       }
     }
   }
-  const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     if (t < T) {
       float s = wave_sum(acc[t]);
-      if (lane == 0) logits[(size_t)t * E + e] = s + b;
+      if (lane == 0) part[wave][t] = s;
     }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const float s = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    logits[(size_t)tid * E + e] = s + (bias ? bias[e] : 0.0f);
   }
 }
 
@@ -101,7 +116,7 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
                                 const float* bias, float* logits, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (T <= kRouterGemvMaxT) {
-    dim3 grid((s.E + 3) / 4);
+    dim3 grid(s.E);
     if (T == 1)
       hipLaunchKernelGGL(router_gemv_kernel<1>, grid, dim3(256), 0, st, x, T, s.d, wr, bias, s.E, logits);
     else if (T <= 4)
@@ -116,13 +131,15 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
 }
 
 // ---------------------------------------------------------------- top-k + gates
-// One wave per token. Round r selects the best element strictly below the
-// previous selection in the order (value descending, index ascending), so no
-// mask is needed; NaN ranks as -inf so a valid index is always chosen.
+// One wave per token; the token's logits are read once into registers. Round
+// r selects the best element strictly below the previous selection in the
+// order (value descending, index ascending), so no mask is needed; NaN ranks
+// as -inf so a valid index is always chosen.
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
+template <int V>  // logits per lane: E <= 64 * V
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
@@ -131,17 +148,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
   const float NEG_INF = -__builtin_huge_valf();
+  float v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane + 64 * j;
+    float a = (e < E) ? row[e] : NEG_INF;
+    v[j] = (a != a) ? NEG_INF : a;  // NaN ranks as -inf
+  }
   float pv = __builtin_huge_valf();  // previous selection (value, index)
   int pi = -1;
   float myv = NEG_INF;  // lane r keeps the value of selection r
   for (int r = 0; r < k; ++r) {
     float bv = NEG_INF;
     int bi = 0x7fffffff;
-    for (int e = lane; e < E; e += 64) {
-      float v = row[e];
-      if (v != v) v = NEG_INF;
-      bool below = (v < pv) || (v == pv && e > pi);
-      if (below && better(v, e, bv, bi)) { bv = v; bi = e; }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int e = lane + 64 * j;
+      const bool below = (v[j] < pv) || (v[j] == pv && e > pi);
+      if (e < E && below && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -163,7 +187,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,
                        hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+  dim3 grid((T + 3) / 4);
+  if (s.E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+  else if (s.E <= 1024)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+  else
+    hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
   return hipGetLastError();
 }
 
