@@ -76,21 +76,33 @@ typedef struct {
  * valid and unchanged until k3moe_destroy; the library never writes or
  * frees them. Every pointer must be 16-byte aligned.
  *
- * MXFP4 layout (OCP Microscaling v1.0, E2M1 elements + E8M0 block scales):
- * a matrix is [rows][K] with K the reduction dimension, stored as
- *   codes  [rows][K/2]  uint8: element 2i in the low nibble, 2i+1 in the high
- *   scales [rows][K/32] uint8: E8M0 byte b means 2^(b-127); 0xFF is NaN
- * and the experts of one tensor are stacked: expert e starts at
- * e * rows * K/2 (codes) and e * rows * K/32 (scales). */
+ * MXFP4 (OCP Microscaling v1.0): E2M1 element codes with one E8M0 scale (byte
+ * b means 2^(b-127), 0xFF is NaN) per 32 consecutive elements along K, the
+ * reduction dimension; within a 32-element block, element 2i sits in the low
+ * nibble of byte i. Expert matrices are stored in the TILED layout below
+ * (k3moe_pack_mxfp4 builds it from the row-major layout codes [rows][K/2],
+ * scales [rows][K/32]). For a matrix of R rows and K columns, RT = R/16,
+ * KT = K/128, KG = ceil(KT/4):
+ *   codes  : 16-row x 128-column tiles, tile (rt, kt) = 1024 bytes at offset
+ *            (rt*KT + kt)*1024; in it, bytes [16*l, 16*l+16) with
+ *            l = r + 16*g hold the block of row 16*rt + r, columns
+ *            128*kt + 32*g .. +31;
+ *   scales : groups of four K tiles, group (rt, kg) = 256 bytes at offset
+ *            (rt*KG + kg)*256; in it, byte 4*l + j (l = r + 16*g) is the scale
+ *            of the block of row 16*rt + r, columns 128*(4*kg+j) + 32*g .. +31
+ *            (127 where 4*kg + j >= KT).
+ * The E experts of one tensor are stacked: expert e's codes start at
+ * e*R*K/2, its scales at e*RT*KG*256. One 1024-byte tile is one wave's
+ * 16-byte-per-lane load and exactly one A operand of the gfx950 MX MFMA. */
 typedef struct {
   const float*   router_w;  /* [E][d] fp32, row-major */
   const float*   router_b;  /* [E] fp32 added to every token's logits, or NULL */
-  const uint8_t* gate_q;    /* [E][f][d/2]  gate projection codes (rows = f, K = d) */
-  const uint8_t* gate_s;    /* [E][f][d/32] gate projection scales */
-  const uint8_t* up_q;      /* [E][f][d/2]  up projection codes */
-  const uint8_t* up_s;      /* [E][f][d/32] */
-  const uint8_t* down_q;    /* [E][d][f/2]  down projection codes (rows = d, K = f) */
-  const uint8_t* down_s;    /* [E][d][f/32] */
+  const uint8_t* gate_q;    /* gate projection codes, tiled, R = f, K = d */
+  const uint8_t* gate_s;    /* gate projection scales, tiled */
+  const uint8_t* up_q;      /* up projection codes, tiled, R = f, K = d */
+  const uint8_t* up_s;      /* up projection scales, tiled */
+  const uint8_t* down_q;    /* down projection codes, tiled, R = d, K = f */
+  const uint8_t* down_s;    /* down projection scales, tiled */
 } k3moe_weights;
 
 /* Create a handle on HIP device `device`: validates cfg and w, checks free
@@ -151,6 +163,18 @@ int k3moe_experts_forward(k3moe* h, const void* x, int32_t T,
                           const int32_t* idx, const float* gate, float* y,
                           void* stream);
 
+/* Rearrange n stacked MXFP4 matrices from the row-major layout (codes
+ * [n][R][K/2], scales [n][R][K/32]) into the tiled layout of k3moe_weights.
+ * Requires R % 16 == 0, K % 128 == 0, n >= 1; tiled_codes needs n*R*K/2 bytes,
+ * tiled_scales k3moe_tiled_scale_bytes(n, R, K) bytes; all four are DEVICE
+ * pointers on the current HIP device, 16-byte aligned and non-overlapping.
+ * Enqueued on `stream`; returns K3MOE_EINVAL for bad arguments. */
+int k3moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t R, int32_t K,
+                     uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream);
+
+/* Bytes of tiled scales for n matrices of R x K (0 if the shape is invalid). */
+int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K);
+
 /* Stage timing, a profiling aid. Between k3moe_profile_begin and
  * k3moe_profile_end every forward records a HIP event before and after each
  * stage's kernel launch(es) on the call's own stream, for at most max_calls
@@ -163,8 +187,8 @@ int k3moe_experts_forward(k3moe* h, const void* x, int32_t T,
 #define K3MOE_STAGE_GROUP         2  /* histogram, scan, permute (three kernels) */
 #define K3MOE_STAGE_QUANT_X       3  /* activation split for the MFMA path (one kernel) */
 #define K3MOE_STAGE_GATEUP        4  /* gate/up projection + SwiGLU (one kernel) */
-#define K3MOE_STAGE_CLEAR_Y       5  /* output clear before scatter-add (one kernel) */
-#define K3MOE_STAGE_DOWN          6  /* down projection + combine (one kernel) */
+#define K3MOE_STAGE_COMBINE       5  /* gate-weighted sum of the k expert outputs (one kernel) */
+#define K3MOE_STAGE_DOWN          6  /* down projection (one kernel; decode: fused with the combine) */
 #define K3MOE_NUM_STAGES          7
 int k3moe_profile_begin(k3moe* h, int32_t max_calls);
 int k3moe_profile_end(k3moe* h, float* total_ms, int32_t* launches);

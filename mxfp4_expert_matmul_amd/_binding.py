@@ -85,6 +85,14 @@ def load_library():
     lib.k3moe_group.restype = ctypes.c_int
     lib.k3moe_experts_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.k3moe_experts_forward.restype = ctypes.c_int
+    lib.k3moe_pack_mxfp4.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.k3moe_pack_mxfp4.restype = ctypes.c_int
+    lib.k3moe_tiled_scale_bytes.argtypes = [i32, i32, i32]
+    lib.k3moe_tiled_scale_bytes.restype = i64
+    lib.k3moe_profile_begin.argtypes = [vp, i32]
+    lib.k3moe_profile_begin.restype = ctypes.c_int
+    lib.k3moe_profile_end.argtypes = [vp, vp, vp]
+    lib.k3moe_profile_end.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -155,6 +163,33 @@ def k3moe_experts_forward(handle, x, idx, gate, y, stream=None):
     rc = load_library().k3moe_experts_forward(handle, _ptr(x), x.shape[0], _ptr(idx), _ptr(gate),
                                               _ptr(y), _stream(stream, x.device))
     _check(rc, "k3moe_experts_forward")
+
+
+def k3moe_tiled_scale_bytes(n: int, R: int, K: int) -> int:
+    return int(load_library().k3moe_tiled_scale_bytes(n, R, K))
+
+
+def k3moe_pack_mxfp4(codes, scales, n, R, K, tiled_codes, tiled_scales, stream=None):
+    rc = load_library().k3moe_pack_mxfp4(_ptr(codes), _ptr(scales), n, R, K, _ptr(tiled_codes),
+                                         _ptr(tiled_scales), _stream(stream, codes.device))
+    _check(rc, "k3moe_pack_mxfp4")
+
+
+def pack_mxfp4(codes, scales, n, R, K):
+    """Row-major device tensors -> new tiled device tensors (flat uint8)."""
+    import torch
+    tc = torch.empty(n * R * K // 2, dtype=torch.uint8, device=codes.device)
+    ts = torch.empty(k3moe_tiled_scale_bytes(n, R, K), dtype=torch.uint8, device=codes.device)
+    k3moe_pack_mxfp4(codes, scales, n, R, K, tc, ts)
+    return tc, ts
+
+
+def pack_layer_weights(w: dict, E: int, d: int, f: int) -> dict:
+    """Row-major layer weights on the device -> tiled copies (other entries kept)."""
+    out = dict(w)
+    for name, (R, K) in (("gate", (f, d)), ("up", (f, d)), ("down", (d, f))):
+        out[name + "_q"], out[name + "_s"] = pack_mxfp4(w[name + "_q"], w[name + "_s"], E, R, K)
+    return out
 
 
 class Layer:

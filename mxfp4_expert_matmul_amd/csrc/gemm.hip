@@ -119,38 +119,38 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c)
 }
 
 // ------------------------------------------------------------- grouped GEMM
-// One workgroup = 4 waves = one (tile, row block): up to kTileM tokens of one
-// expert (a tile of the grouped pairs) times kRowsPerBlock weight rows.
-//   gate/up (kMode = kGateUp): each wave owns 32 features, i.e. two 16-row
-//     MFMA tiles of the gate matrix and the same two of the up matrix, so
-//     SwiGLU pairs sit in the same lanes; a block covers 128 features.
-//   down (kMode = kDown): each wave owns 64 output rows (four 16-row tiles);
-//     a block covers 256 rows.
-// The K dimension is walked in chunks of 8 MX blocks (256 elements; a last
-// chunk of 4 blocks when K/32 is not a multiple of 8). Per chunk:
-//   * activations (two E4M3 terms) of the tile's tokens are copied once per
-//     workgroup straight from global memory into LDS (global_load_lds, 16
-//     bytes per lane, four 256-byte token rows per wave instruction) and read
-//     by every wave as MFMA B operands; double-buffered. Within a token row
-//     the 16-byte piece p is stored at slot p ^ (row % 16), so the 16 lanes
-//     of an MFMA column group (16 consecutive rows, same piece) read 16
-//     distinct bank groups; the scales go through registers;
-//   * each wave's weight rows are loaded straight into registers one chunk
-//     ahead (two contiguous MX blocks per lane, 128 contiguous bytes per row).
-// Physical block of MFMA slot-block kappa at step s of a chunk with S steps
-// = chunk base + S*kappa + s.
+// One workgroup = 8 waves = one (tile, row block): up to kTileM tokens of one
+// expert (a tile of the grouped pairs) times a block of weight rows.
+//   gate/up (kGateUp): 128 features = 128 gate rows + the same 128 up rows;
+//   down    (kDown):   256 output rows.
+// Waves are laid out 4 (along rows) x 2 (along tokens): wave (nw, mw) owns 32
+// features (gate/up: two 16-row MFMA tiles of gate and the same two of up, so
+// SwiGLU pairs sit in one lane) or 64 rows (down: four 16-row tiles), for the
+// 64 tokens 64 mw .. 64 mw + 63 (four 16-column MFMA tiles).
+//
+// Weights (tiled layout, layout.hip) go straight to registers: one MFMA A
+// operand is one 1 KB tile, read with one coalesced 16-byte-per-lane load,
+// one chunk ahead of the MFMAs; a scale dword per lane covers 4 K tiles.
+// Activations (two E4M3 terms + scales) of the tile's tokens are copied once
+// per workgroup straight into LDS (global_load_lds, four 256-byte token rows
+// per wave instruction; piece p of token row t at slot p ^ (t % 16) so an
+// MFMA column group reads 16 distinct bank groups), double-buffered.
+// K is walked in chunks of two 128-column tiles (a last chunk of one tile
+// when K/128 is odd); MFMA step s of chunk c is K tile 2c + s, and MFMA
+// slot-block kappa is that tile's 32-column block kappa.
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
-constexpr int kChunkBlocks = 8;                 // MX blocks per K chunk
-constexpr int kActRow = kChunkBlocks * 32;      // LDS bytes per token row and term
-constexpr int kColTiles = kTileM / 16;
+constexpr int kChunkTiles = 2;                  // K tiles (128 columns) per chunk
+constexpr int kActRow = kChunkTiles * 128;      // LDS bytes per token row and term
+constexpr int kScRow = kChunkTiles * 4;         // LDS scale bytes per token row and term
+constexpr int kThreads = 512;
 
 template <int MODE>
 struct GemmShape {
   static constexpr int NM = (MODE == kGateUp) ? 2 : 1;   // weight matrices
   static constexpr int NRT = (MODE == kGateUp) ? 2 : 4;  // 16-row tiles per matrix per wave
-  static constexpr int kRowsPerWave = NM * NRT * 16 / NM;  // output rows per wave (per matrix)
-  static constexpr int kRowsPerBlock = 4 * kRowsPerWave;
+  static constexpr int kRowsPerWave = NRT * 16;           // output rows (features) per wave
+  static constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // output rows per workgroup
 };
 
 struct TileInfo {
@@ -181,8 +181,13 @@ __device__ __forceinline__ bool load_tile(int tile, const int32_t* tiles, const 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+struct ActLds {
+  uint8_t a[2][kTileM][kActRow];  // activation terms, swizzled
+  uint8_t s[2][kTileM][kScRow];   // activation scales (E8M0), per 32-column block
+};
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
+__global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
     int K, int nrows, int f_out, int k, const uint8_t* __restrict__ wq0,
     const uint8_t* __restrict__ ws0, const uint8_t* __restrict__ wq1,
     const uint8_t* __restrict__ ws1, const uint8_t* __restrict__ act_hi,
@@ -191,11 +196,14 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, int nrb, uint8_t* __restrict__ out_hi,
     uint8_t* __restrict__ out_lo, uint8_t* __restrict__ outs_hi, uint8_t* __restrict__ outs_lo,
-    const float* __restrict__ gate, float* __restrict__ y) {
+    float* __restrict__ slots) {
   using G = GemmShape<MODE>;
   constexpr int NM = G::NM, NRT = G::NRT;
-  __shared__ __attribute__((aligned(16))) uint8_t act_lds[2][2][kTileM][kActRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2][2][kTileM][kChunkBlocks];
+  constexpr int NCT = 4;  // 16-token MFMA column tiles per wave
+  // two separately named buffers (not an array indexed by a runtime number)
+  // so reads of one need not wait for the direct-to-LDS loads filling the other
+  __shared__ __attribute__((aligned(16))) ActLds lds0;
+  __shared__ __attribute__((aligned(16))) ActLds lds1;
   __shared__ int tok_lds[kTileM];
 
   int tile, rb;
@@ -204,11 +212,14 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
   if (!load_tile(tile, tiles, ntiles, offsets, ti)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int nw = wave & 3, mw = wave >> 2;
   const int r = lane & 15, g = lane >> 4;
-  const int nb = K >> 5;
-  const int nct = (ti.cnt + 15) >> 4;
-  const int w0 = rb * G::kRowsPerBlock + wave * G::kRowsPerWave;  // first row of this wave
-  const bool wave_on = w0 < nrows;
+  const int nb = K >> 5, KT = K >> 7, KG = (KT + 3) >> 2, RT = nrows >> 4;
+  const int row_base = rb * G::kRowsPerBlock;          // first output row of the block
+  const int w0 = row_base + nw * G::kRowsPerWave;       // first output row of this wave
+  const int m0 = 64 * mw;                               // first tile token of this wave
+  const int nct = max(0, min(NCT, (ti.cnt - m0 + 15) >> 4));  // token tiles of this wave
+  const bool wave_on = (w0 < nrows) && (nct > 0);
 
   // activation row (token for gate/up, sorted pair position for down) per tile row
   if (tid < kTileM) {
@@ -217,151 +228,155 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
   }
   __syncthreads();
 
-  // weight addressing: uniform per-expert bases + one 32-bit lane offset
-  // (rows clamped into range for waves past the end)
-  const size_t qstride = (size_t)(K >> 1);
-  const uint8_t* wqb[NM];
-  const uint8_t* wsb[NM];
-  wqb[0] = wq0 + (size_t)ti.e * nrows * qstride;
-  wsb[0] = ws0 + (size_t)ti.e * nrows * nb;
-  if (NM == 2) {
-    wqb[NM - 1] = wq1 + (size_t)ti.e * nrows * qstride;
-    wsb[NM - 1] = ws1 + (size_t)ti.e * nrows * nb;
-  }
-  const int row_l = (wave_on ? w0 : 0) + r;
-  const uint32_t qoff = (uint32_t)row_l * (uint32_t)(K >> 1);
-  const uint32_t soff = (uint32_t)row_l * (uint32_t)nb;
-
-  // activations of one chunk straight into LDS: wave instruction I (8 per
-  // wave) moves term I / 16, rows 4 (I % 16) .. +3, lane l -> row + l / 16,
-  // slot l % 16 holding piece (l % 16) ^ (row % 16). Row groups past the
-  // tile's tokens are skipped; pieces past a 4-block tail chunk re-read
-  // pieces of the chunk (their slots are never read).
-  auto act_issue = [&](int buf, int kb0, int cblocks) {
+  // ---- weights: tile (rt, kt) of matrix m at wq[m] + ((e RT + rt) KT + kt) 1024 + 16 lane
+  const int rt0 = (wave_on ? w0 : 0) >> 4;  // first row tile of this wave
+  const uint8_t* wq_t[NM];
+  const uint32_t* ws_t[NM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int I = wave * 8 + i;
-      const int term = I >> 4, row0 = 4 * (I & 15);
-      if (row0 < ti.cnt) {
-        const int row = row0 + (lane >> 4);
-        int piece = (lane & 15) ^ (row & 15);
-        if (cblocks < kChunkBlocks) piece &= 2 * cblocks - 1;
-        const uint8_t* src =
-            (term ? act_lo : act_hi) + (size_t)tok_lds[row] * K + 32 * kb0 + 16 * piece;
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)&act_lds[buf][term][row0][0], 16, 0, 0);
-      }
-    }
-  };
-  auto sc_load = [&](int kb0, int cblocks) {
-    uint2 v = make_uint2(0u, 0u);
-    if (tid < 2 * kTileM) {
-      const int term = tid >> 6, tk = tid & 63;
-      if (tk < ti.cnt) {
-        const uint8_t* src = (term ? acts_lo : acts_hi) + (size_t)tok_lds[tk] * nb + kb0;
-        if (cblocks == kChunkBlocks)
-          v = *reinterpret_cast<const uint2*>(src);
-        else
-          v.x = *reinterpret_cast<const uint32_t*>(src);
-      }
-    }
-    return v;
-  };
-  auto sc_store = [&](int buf, uint2 v) {
-    if (tid < 2 * kTileM) *reinterpret_cast<uint2*>(&sc_lds[buf][tid >> 6][tid & 63][0]) = v;
-  };
-
-  // weights of one chunk: S contiguous blocks per lane per row tile
+  for (int m = 0; m < NM; ++m) {
+    const uint8_t* q = (m == 0) ? wq0 : wq1;
+    const uint8_t* sc = (m == 0) ? ws0 : ws1;
+    wq_t[m] = q + (((size_t)ti.e * RT + rt0) * KT) * 1024 + 16 * lane;
+    ws_t[m] = reinterpret_cast<const uint32_t*>(sc + (((size_t)ti.e * RT + rt0) * KG) * 256) + lane;
+  }
   struct WStage {
-    uint4 q[NM][NRT][2];
-    int s[NM][NRT];
+    uint4 q[NM][NRT][kChunkTiles];
   };
-  auto w_load = [&](int kb0, int S, WStage& ws) {
+  auto w_load = [&](int c, int S, WStage& ws) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const uint8_t* p = wqb[m] + 16 * rt * qstride + qoff + 16 * (kb0 + S * g);
-        const uint8_t* ps = wsb[m] + 16 * rt * nb + soff + kb0 + S * g;
-        ws.q[m][rt][0] = *reinterpret_cast<const uint4*>(p);
-        if (S == 2) {
-          ws.q[m][rt][1] = *reinterpret_cast<const uint4*>(p + 16);
-          ws.s[m][rt] = *reinterpret_cast<const uint16_t*>(ps);
-        } else {
-          ws.s[m][rt] = *ps;
-        }
-      }
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int s = 0; s < kChunkTiles; ++s)
+          if (s < S)
+            ws.q[m][rt][s] = *reinterpret_cast<const uint4*>(
+                wq_t[m] + ((size_t)rt * KT + kChunkTiles * c + s) * 1024);
+  };
+  int sw[NM][NRT];  // scale dwords of the current group of 4 K tiles
+  auto s_load = [&](int kg) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) sw[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
   };
 
-  v4f acc[NM][NRT][kColTiles];
+  // ---- activations: wave instruction j = 8 wave + i (64 per chunk): term
+  // j / 32, token rows 4 (j % 32) .. +3; lane -> row + lane / 16, slot lane % 16
+  // holding piece slot ^ (row % 16). Scales: one 4-byte copy per lane, wave w
+  // -> term w / 4, rows 32 (w % 4) + lane / 2, half lane % 2.
+  const uint8_t* act_t = (wave < 4) ? act_hi : act_lo;
+  uint32_t asrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 8 * wave + i;
+    const int row = 4 * (j & 31) + (lane >> 4);
+    asrc[i] = (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+  }
+  const int sc_row = 32 * (wave & 3) + (lane >> 1);
+  const uint8_t* sc_src = ((wave < 4) ? acts_hi : acts_lo) + (size_t)tok_lds[sc_row] * nb;
+  auto act_issue = [&](ActLds& L, int c, int S) {
+    const uint32_t kb = (uint32_t)(kChunkTiles * c) * 128u;  // first column of the chunk
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 8 * wave + i;
+      const int term = j >> 5, row0 = 4 * (j & 31);
+      if (row0 < ti.cnt) {
+        uint32_t off = asrc[i] + kb;
+        if (S < kChunkTiles) off -= 16u * (((lane & 15) ^ ((row0 + (lane >> 4)) & 15)) & 8u);
+        __builtin_amdgcn_global_load_lds(act_t + off, (lds_ptr)&L.a[term][row0][0], 16, 0, 0);
+      }
+    }
+    {
+      const int half = (S < kChunkTiles) ? 0 : (lane & 1);
+      __builtin_amdgcn_global_load_lds(sc_src + (kb >> 5) + 4 * half,
+                                       (lds_ptr)&L.s[wave >> 2][32 * (wave & 3)][0], 4, 0, 0);
+    }
+  };
+
+  v4f acc[NM][NRT][NCT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < NCT; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // one chunk of MFMAs from LDS buffer `buf` with weights `ws`
-  auto compute = [&](int buf, int S, const WStage& ws) {
+  // one chunk of MFMAs; SEL = byte of the scale dwords for step 0 (0 or 2)
+  auto compute = [&](const ActLds& L, int S, const WStage& ws, int sel) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kChunkTiles; ++s) {
       if (s >= S) break;
-      // pieces of slot-blocks g/2 and 2 + g/2, swizzled by the row (row % 16 == r)
-      const int c0 = 16 * ((2 * (S * (g >> 1) + s) + (g & 1)) ^ r);
-      const int c1 = 16 * ((2 * (S * (2 + (g >> 1)) + s) + (g & 1)) ^ r);
-      const int sb = S * g + s;  // scale block of this lane
+      // pieces of slot-blocks g/2 and 2 + g/2 of tile s (token row % 16 == r)
+      const int c0 = 16 * ((8 * s + g) ^ r);
+      const int c1 = 16 * ((8 * s + 4 + g) ^ r);
+      const int sb = 4 * s + g;
 #pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         if (ct < nct) {
-          const int tr = 16 * ct + r;
-          const v8i bh = fp8_operand(*reinterpret_cast<const uint4*>(&act_lds[buf][0][tr][c0]),
-                                     *reinterpret_cast<const uint4*>(&act_lds[buf][0][tr][c1]));
-          const v8i bl = fp8_operand(*reinterpret_cast<const uint4*>(&act_lds[buf][1][tr][c0]),
-                                     *reinterpret_cast<const uint4*>(&act_lds[buf][1][tr][c1]));
-          const int sh = sc_lds[buf][0][tr][sb];
-          const int sl = sc_lds[buf][1][tr][sb];
+          const int tr = m0 + 16 * ct + r;
+          const v8i bh = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
+                                     *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
+          const v8i bl = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
+                                     *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
+          const int sh = L.s[0][tr][sb];
+          const int sl = L.s[1][tr][sb];
 #pragma unroll
           for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
               const v8i a = fp4_operand(ws.q[m][rt][s]);
-              if (s == 0) {
-                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, ws.s[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, ws.s[m][rt], bl, sl, acc[m][rt][ct]);
+              // scale byte (sel + s) of the A scale dword
+              if (sel + s == 0) {
+                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
+                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
+              } else if (sel + s == 1) {
+                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
+                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
+              } else if (sel + s == 2) {
+                acc[m][rt][ct] = mfma_fp4_fp8<2>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
+                acc[m][rt][ct] = mfma_fp4_fp8<2>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
               } else {
-                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, ws.s[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, ws.s[m][rt], bl, sl, acc[m][rt][ct]);
+                acc[m][rt][ct] = mfma_fp4_fp8<3>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
+                acc[m][rt][ct] = mfma_fp4_fp8<3>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
               }
             }
         }
+        // keep one column tile's B fragments live at a time
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  const int nfull = nb / kChunkBlocks;
-  const bool tail = (nb % kChunkBlocks) != 0;  // one last chunk of 4 blocks
-  const int nchunks = nfull + (tail ? 1 : 0);
-  WStage wcur, wnxt;
-  {
-    const int cb = (nfull > 0) ? kChunkBlocks : 4;
-    act_issue(0, 0, cb);
-    w_load(0, cb / 4, wcur);
-    sc_store(0, sc_load(0, cb));
-  }
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int S = (c < nfull) ? 2 : 1;
-    const bool more = (c + 1) < nchunks;
-    const int cb_next = ((c + 1) < nfull) ? kChunkBlocks : 4;
-    uint2 scn = make_uint2(0u, 0u);
-    if (more) {
-      act_issue((c + 1) & 1, (c + 1) * kChunkBlocks, cb_next);
-      w_load((c + 1) * kChunkBlocks, cb_next / 4, wnxt);
-      scn = sc_load((c + 1) * kChunkBlocks, cb_next);
+  // K loop, two chunks (= one scale group of 4 K tiles) per iteration so each
+  // LDS buffer and each scale byte is named statically.
+  const int nchunks = (KT + kChunkTiles - 1) / kChunkTiles;
+  auto tiles_of = [&](int c) { return min(kChunkTiles, KT - kChunkTiles * c); };
+  WStage wa, wb;
+  act_issue(lds0, 0, tiles_of(0));
+  if (wave_on) w_load(0, tiles_of(0), wa);
+  __syncthreads();  // also waits for this thread's direct-to-LDS loads
+  for (int c = 0; c < nchunks; c += 2) {
+    if (wave_on) s_load(c >> 1);
+    {  // even chunk c: buffer 0, weights wa, scale bytes 0/1
+      const bool more = (c + 1) < nchunks;
+      if (more) {
+        act_issue(lds1, c + 1, tiles_of(c + 1));
+        if (wave_on) w_load(c + 1, tiles_of(c + 1), wb);
+      }
+      if (wave_on) compute(lds0, tiles_of(c), wa, 0);
+      __syncthreads();
+      if (!more) break;
     }
-    if (wave_on) compute(c & 1, S, wcur);
-    if (more) sc_store((c + 1) & 1, scn);
-    __syncthreads();  // also waits for this thread's direct-to-LDS loads
-    wcur = wnxt;
+    {  // odd chunk c + 1: buffer 1, weights wb, scale bytes 2/3
+      const bool more = (c + 2) < nchunks;
+      if (more) {
+        act_issue(lds0, c + 2, tiles_of(c + 2));
+        if (wave_on) w_load(c + 2, tiles_of(c + 2), wa);
+      }
+      if (wave_on) compute(lds1, tiles_of(c + 1), wb, 2);
+      __syncthreads();
+    }
   }
   if (!wave_on) return;
 
@@ -371,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
     // of token column r).
     const int nbf = f_out >> 5;
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       if (ct >= nct) continue;
       float h[2][4];
       float amax = 0.0f;
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
       ramax = fmaxf(ramax, __shfl_xor(ramax, 32, 64));
       const uint32_t b2 = e4m3_block_scale_byte(ramax);
       const float s2inv = e8m0_to_f32(254u - b2);
-      const int i = 16 * ct + r;
+      const int i = m0 + 16 * ct + r;
       if (i < ti.cnt) {
         const size_t pos = (size_t)ti.base + ti.row0 + i;
 #pragma unroll
@@ -419,36 +434,45 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(
       }
     }
   } else {
-    // y[t, m] += gate[pair] * acc: lane (r, g) holds rows w0 + 16 rt + 4 g + q
-    // of token column r.
+    // this pair's expert output, rows w0 + 16 rt + 4 g + q of token column r,
+    // stored in the pair's own slot (no atomics; summed per token later)
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       if (ct >= nct) continue;
-      const int i = 16 * ct + r;
+      const int i = m0 + 16 * ct + r;
       if (i >= ti.cnt) continue;
       const int pair = perm[ti.base + ti.row0 + i];
-      const int tok = pair / k;
-      const float gw = gate[pair];
-      float* yr = y + (size_t)tok * nrows + w0 + 4 * g;
+      float* o = slots + (size_t)pair * nrows + w0 + 4 * g;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) atomicAdd(yr + 16 * rt + q, gw * acc[0][rt][ct][q]);
+        *reinterpret_cast<float4*>(o + 16 * rt) =
+            make_float4(acc[0][rt][ct][0], acc[0][rt][ct][1], acc[0][rt][ct][2], acc[0][rt][ct][3]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-hipError_t launch_clear_y(float* y, int T, int d, hipStream_t st) {
-  const size_t n4 = (size_t)T * d / 4;
-  if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 4096)),
-                     dim3(256), 0, st, reinterpret_cast<float4*>(y), n4);
-  return hipGetLastError();
+// y[t] = sum_j gate[t,j] * slot[t*k + j], j in order; pairs whose expert is
+// outside [0, E) contribute zero. One thread per 4 outputs.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slots,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ gate, int T,
+                                                      int d, int k, int E, float* __restrict__ y) {
+  const int d4 = d >> 2;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * d4) return;
+  const int t = (int)(i / d4), c = (int)(i % d4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[(size_t)t * k + j];
+    if (e < 0 || e >= E) continue;
+    const float gw = gate[(size_t)t * k + j];
+    const float4 v = reinterpret_cast<const float4*>(slots + ((size_t)t * k + j) * d)[c];
+    acc.x = fmaf(gw, v.x, acc.x);
+    acc.y = fmaf(gw, v.y, acc.y);
+    acc.z = fmaf(gw, v.z, acc.z);
+    acc.w = fmaf(gw, v.w, acc.w);
+  }
+  reinterpret_cast<float4*>(y)[i] = acc;
 }
 
 static unsigned gemm_grid(int max_tiles, int nrb) {
@@ -464,26 +488,35 @@ hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, con
   const size_t xplane = (size_t)T * s.d, xsplane = (size_t)T * (s.d / 32);
   const size_t hplane = P * s.f, hsplane = P * (s.f / 32);
   const int nrb = s.f / GemmShape<kGateUp>::kRowsPerBlock;
-  hipLaunchKernelGGL(mx_gemm_kernel<kGateUp>, dim3(gemm_grid(max_tiles, nrb)), dim3(256), 0, st,
-                     s.d, s.f, s.f, s.k, w.gate_q, w.gate_s, w.up_q, w.up_s, xq, xq + xplane, xs,
-                     xs + xsplane, offsets, perm, tiles, ntiles, nrb, hq, hq + hplane, hs,
-                     hs + hsplane, nullptr, nullptr);
+  hipLaunchKernelGGL(mx_gemm_kernel<kGateUp>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
+                     st, s.d, s.f, s.f, s.k, w.gate_q, w.gate_s, w.up_q, w.up_s, xq, xq + xplane,
+                     xs, xs + xsplane, offsets, perm, tiles, ntiles, nrb, hq, hq + hplane, hs,
+                     hs + hsplane, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const float* gate,
-                            const int32_t* offsets, const int32_t* perm, const int32_t* tiles,
-                            const int32_t* ntiles, int max_tiles, const uint8_t* hq,
-                            const uint8_t* hs, float* y, hipStream_t st) {
+hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* offsets,
+                            const int32_t* perm, const int32_t* tiles, const int32_t* ntiles,
+                            int max_tiles, const uint8_t* hq, const uint8_t* hs, float* slots,
+                            hipStream_t st) {
   if (T <= 0 || max_tiles <= 0) return hipSuccess;
   const size_t P = (size_t)T * s.k;
   const size_t hplane = P * s.f, hsplane = P * (s.f / 32);
   constexpr int rpb = GemmShape<kDown>::kRowsPerBlock;
   const int nrb = (s.d + rpb - 1) / rpb;
-  hipLaunchKernelGGL(mx_gemm_kernel<kDown>, dim3(gemm_grid(max_tiles, nrb)), dim3(256), 0, st,
-                     s.f, s.d, s.f, s.k, w.down_q, w.down_s, nullptr, nullptr, hq, hq + hplane, hs,
-                     hs + hsplane, offsets, perm, tiles, ntiles, nrb, nullptr, nullptr, nullptr,
-                     nullptr, gate, y);
+  hipLaunchKernelGGL(mx_gemm_kernel<kDown>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
+                     st, s.f, s.d, s.f, s.k, w.down_q, w.down_s, nullptr, nullptr, hq, hq + hplane,
+                     hs, hs + hsplane, offsets, perm, tiles, ntiles, nrb, nullptr, nullptr, nullptr,
+                     nullptr, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* slots, const int32_t* idx, const float* gate, int T,
+                          const Shape& s, float* y, hipStream_t st) {
+  const size_t n = (size_t)T * (s.d / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, slots,
+                     idx, gate, T, s.d, s.k, s.E, y);
   return hipGetLastError();
 }
 

@@ -1,11 +1,12 @@
-// Decode path (few tokens): the expert FFNs as bandwidth-bound MXFP4 GEMVs.
+// Decode path (few tokens): the expert FFNs as bandwidth-bound MXFP4 GEMVs
+// over the tiled MXFP4 layout (see layout.hip).
 // Prior art: the pages' MXFP4 matmul works on the packed nibbles directly and
 // never materialises a dequantised expert (kimi-k3-in-c CHANGELOG walk-through,
 // 0.1.0 section). Here each lane loads whole 32-element MX blocks (16 bytes of
-// E2M1 codes + 1 E8M0 byte) with coalesced 16-byte loads, decodes nibble
-// pairs in registers with the gfx950 FP4->bf16 convert, accumulates with
-// bf16 dot products into fp32, applies the block scale once per block and
-// reduces across the wave.
+// E2M1 codes) with coalesced 16-byte loads (a wave reads one 1 KB tile),
+// decodes nibble pairs in registers with the gfx950 FP4 converts,
+// accumulates in fp32, applies the E8M0 block scale once per block and sums
+// each row over its four lane groups.
 //
 //   gemv_gateup: per (token, slot) pair and feature n:
 //       g = Wg[e][n,:] . x,  u = Wu[e][n,:] . x,  h[n] = SiLU(g) * u   (fp32)
@@ -58,186 +59,147 @@ __device__ __forceinline__ float block_dot_f32(const uint4 q, const float* hv) {
   return acc;
 }
 
-constexpr int kGateUpRowsPerWave = 4;
-
-// grid: (T*k pairs, ceil(f / (4 * kGateUpRowsPerWave))), block 256.
-// NBL = MX blocks of the reduction dim handled per lane (ceil((d/32)/64)).
-template <int NBL>
+// gate/up: one wave per (pair, 16-row tile of gate and of up). Lane (r, g)
+// takes row 16 rt + r, K block g of every 128-column tile, so one 16-byte
+// load per lane reads a whole 1 KB tile; its 32 activations are the same for
+// the 16 lanes of a group (a broadcast load). Rows are summed over the 4
+// groups at the end. Four K tiles per step share one scale dword per lane.
+// grid: (T*k pairs, ceil(f / 64)), block 256 (4 waves = 4 row tiles).
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
     const int32_t* __restrict__ idx, float* __restrict__ h32) {
   const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
   const int pair = blockIdx.x;
+  const int rt = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int RT = f >> 4, KT = d >> 7, KG = (KT + 3) >> 2;
+  if (rt >= RT) return;
   const int t = pair / k;
   const int e = idx[pair];
   if (e < 0 || e >= E) return;  // dropped pair: never read downstream
-  const int nb = d >> 5;
-  // activations of this lane's blocks, as packed bf16 pairs
-  uint32_t xr[NBL][16];
+  const size_t tile0 = ((size_t)e * RT + rt) * KT;
+  const uint8_t* gqt = gq + tile0 * 1024 + 16 * lane;
+  const uint8_t* uqt = uq + tile0 * 1024 + 16 * lane;
+  const size_t grp0 = ((size_t)e * RT + rt) * KG;
+  const uint32_t* gst = reinterpret_cast<const uint32_t*>(gs + grp0 * 256) + lane;
+  const uint32_t* ust = reinterpret_cast<const uint32_t*>(us + grp0 * 256) + lane;
+  const uint16_t* xt = x + (size_t)t * d + 32 * g;
+  float ga = 0.0f, ua = 0.0f;
+  for (int kg = 0; kg < KG; ++kg) {
+    const uint32_t sgw = gst[64 * kg], suw = ust[64 * kg];
+    const int nk = min(4, KT - 4 * kg);
+    uint4 qg[4], qu[4];
+    uint32_t xr[4][16];
 #pragma unroll
-  for (int b = 0; b < NBL; ++b) {
-    const int blk = lane + 64 * b;
-    if (blk < nb) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d + 32 * blk);
+    for (int j = 0; j < 4; ++j) {
+      if (j < nk) {
+        const int kt = 4 * kg + j;
+        qg[j] = *reinterpret_cast<const uint4*>(gqt + (size_t)kt * 1024);
+        qu[j] = *reinterpret_cast<const uint4*>(uqt + (size_t)kt * 1024);
+        const uint4* xs = reinterpret_cast<const uint4*>(xt + 128 * kt);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint4 q = src[v];
-        xr[b][4 * v + 0] = q.x; xr[b][4 * v + 1] = q.y; xr[b][4 * v + 2] = q.z; xr[b][4 * v + 3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) xr[b][v] = 0u;
-    }
-  }
-  const int n0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kGateUpRowsPerWave;
-  const size_t qrow = (size_t)(d >> 1), srow = (size_t)nb;
-  // two row pairs per pass; all of a pass's loads are issued before any math
-#pragma unroll
-  for (int r0 = 0; r0 < kGateUpRowsPerWave; r0 += 2) {
-    uint4 qg[2][NBL], qu[2][NBL];
-    uint32_t sg[2][NBL], su[2][NBL];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int n = min(n0 + r0 + rr, f - 1);
-      const size_t row = (size_t)e * f + n;
-#pragma unroll
-      for (int b = 0; b < NBL; ++b) {
-        const int blk = lane + 64 * b;
-        if (blk < nb) {
-          qg[rr][b] = *reinterpret_cast<const uint4*>(gq + row * qrow + 16 * blk);
-          qu[rr][b] = *reinterpret_cast<const uint4*>(uq + row * qrow + 16 * blk);
-          sg[rr][b] = gs[row * srow + blk];
-          su[rr][b] = us[row * srow + blk];
+        for (int v = 0; v < 4; ++v) {
+          const uint4 q = xs[v];
+          xr[j][4 * v] = q.x; xr[j][4 * v + 1] = q.y; xr[j][4 * v + 2] = q.z; xr[j][4 * v + 3] = q.w;
         }
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int n = n0 + r0 + rr;
-      float ga = 0.0f, ua = 0.0f;
-#pragma unroll
-      for (int b = 0; b < NBL; ++b) {
-        const int blk = lane + 64 * b;
-        if (blk < nb) {
-          ga = fmaf(block_dot_bf16(qg[rr][b], xr[b]), e8m0_to_f32(sg[rr][b]), ga);
-          ua = fmaf(block_dot_bf16(qu[rr][b], xr[b]), e8m0_to_f32(su[rr][b]), ua);
-        }
+    for (int j = 0; j < 4; ++j) {
+      if (j < nk) {
+        ga = fmaf(block_dot_bf16(qg[j], xr[j]), e8m0_to_f32((sgw >> (8 * j)) & 0xffu), ga);
+        ua = fmaf(block_dot_bf16(qu[j], xr[j]), e8m0_to_f32((suw >> (8 * j)) & 0xffu), ua);
       }
-      ga = wave_sum(ga);
-      ua = wave_sum(ua);
-      if (lane == 0 && n < f) h32[(size_t)pair * f + n] = silu_f32(ga) * ua;
     }
   }
+  ga += __shfl_xor(ga, 16, 64);
+  ga += __shfl_xor(ga, 32, 64);
+  ua += __shfl_xor(ua, 16, 64);
+  ua += __shfl_xor(ua, 32, 64);
+  if (g == 0) h32[(size_t)pair * f + 16 * rt + r] = silu_f32(ga) * ua;
 }
 
-constexpr int kDownRowsPerBlock = 16;
-
-// grid: (T, ceil(d / kDownRowsPerBlock)), block 256 (4 waves). Wave w handles
-// slots j = w, w+4, ... of the token for all kDownRowsPerBlock rows; lanes
-// keep gate-weighted partials, reduced once at the end, then the 4 waves are
-// summed in fixed order through LDS.
-template <int NBF>
+// down + combine: workgroup = one token x one 16-row tile of the output; its
+// 4 waves split the token's k slots (wave w: j = w, w+4, ...). Lane (r, g)
+// keeps a gate-weighted partial of row 16 rt + r over K block g of every
+// tile; partials meet across groups, then across waves in fixed order
+// through LDS. Deterministic, no atomics.
+// grid: (T, d / 16), block 256.
 __global__ __launch_bounds__(256) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ h32, float* __restrict__ y) {
-  __shared__ float part[4][kDownRowsPerBlock];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x;
-  const int m0 = blockIdx.y * kDownRowsPerBlock;
-  const int nbf = f >> 5;
-  const size_t qrow = (size_t)(f >> 1), srow = (size_t)nbf;
-  float acc[kDownRowsPerBlock];
-#pragma unroll
-  for (int r = 0; r < kDownRowsPerBlock; ++r) acc[r] = 0.0f;
+  __shared__ float part[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t = blockIdx.x, rt = blockIdx.y;
+  const int RT = d >> 4, KT = f >> 7, KG = (KT + 3) >> 2;
+  float acc = 0.0f;
   for (int j = wave; j < k; j += 4) {
     const int pair = t * k + j;
     const int e = idx[pair];
     if (e < 0 || e >= E) continue;  // dropped pair contributes zero
-    const float g = gate[pair];
-    float hv[NBF][32];
+    const float gw = gate[pair];
+    const size_t tile0 = ((size_t)e * RT + rt) * KT;
+    const uint8_t* qt = dq + tile0 * 1024 + 16 * lane;
+    const uint32_t* st = reinterpret_cast<const uint32_t*>(ds + ((size_t)e * RT + rt) * KG * 256) + lane;
+    const float* ht = h32 + (size_t)pair * f + 32 * g;
+    float pe = 0.0f;
+    for (int kg = 0; kg < KG; ++kg) {
+      const uint32_t sw = st[64 * kg];
+      const int nk = min(4, KT - 4 * kg);
 #pragma unroll
-    for (int b = 0; b < NBF; ++b) {
-      const int blk = lane + 64 * b;
-      if (blk < nbf) {
-        const float4* src = reinterpret_cast<const float4*>(h32 + (size_t)pair * f + 32 * blk);
+      for (int j2 = 0; j2 < 4; j2 += 2) {
+        uint4 q[2];
+        float hv[2][32];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          float4 q = src[v];
-          hv[b][4 * v] = q.x; hv[b][4 * v + 1] = q.y; hv[b][4 * v + 2] = q.z; hv[b][4 * v + 3] = q.w;
+        for (int u = 0; u < 2; ++u) {
+          if (j2 + u < nk) {
+            const int kt = 4 * kg + j2 + u;
+            q[u] = *reinterpret_cast<const uint4*>(qt + (size_t)kt * 1024);
+            const float4* hs = reinterpret_cast<const float4*>(ht + 128 * kt);
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              const float4 h4 = hs[v];
+              hv[u][4 * v] = h4.x; hv[u][4 * v + 1] = h4.y; hv[u][4 * v + 2] = h4.z; hv[u][4 * v + 3] = h4.w;
+            }
+          }
         }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (j2 + u < nk)
+            pe = fmaf(block_dot_f32(q[u], hv[u]), e8m0_to_f32((sw >> (8 * (j2 + u))) & 0xffu), pe);
       }
     }
-    // all rows' loads first, then the math
-    uint4 q[kDownRowsPerBlock][NBF];
-    uint32_t sc[kDownRowsPerBlock][NBF];
-#pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) {
-      const size_t row = (size_t)e * d + min(m0 + r, d - 1);
-#pragma unroll
-      for (int b = 0; b < NBF; ++b) {
-        const int blk = lane + 64 * b;
-        if (blk < nbf) {
-          q[r][b] = *reinterpret_cast<const uint4*>(dq + row * qrow + 16 * blk);
-          sc[r][b] = ds[row * srow + blk];
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kDownRowsPerBlock; ++r) {
-#pragma unroll
-      for (int b = 0; b < NBF; ++b) {
-        const int blk = lane + 64 * b;
-        if (blk < nbf) acc[r] = fmaf(g * e8m0_to_f32(sc[r][b]), block_dot_f32(q[r][b], hv[b]), acc[r]);
-      }
-    }
+    acc = fmaf(gw, pe, acc);
   }
-#pragma unroll
-  for (int r = 0; r < kDownRowsPerBlock; ++r) {
-    float s = wave_sum(acc[r]);
-    if (lane == 0) part[wave][r] = s;
-  }
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (g == 0) part[wave][r] = acc;
   __syncthreads();
-  if (threadIdx.x < kDownRowsPerBlock) {
-    const int m = m0 + threadIdx.x;
-    if (m < d) {
-      float s = part[0][threadIdx.x];
-      s += part[1][threadIdx.x];
-      s += part[2][threadIdx.x];
-      s += part[3][threadIdx.x];
-      y[(size_t)t * d + m] = s;
-    }
+  if (threadIdx.x < 16) {
+    const float s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                    part[3][threadIdx.x];
+    y[(size_t)t * d + 16 * rt + threadIdx.x] = s;
   }
 }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
                               const int32_t* idx, float* h32, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const int nbl = (s.d / 32 + 63) / 64;
-  dim3 g1(T * s.k, (s.f + 4 * kGateUpRowsPerWave - 1) / (4 * kGateUpRowsPerWave));
-#define K3_GU(N) hipLaunchKernelGGL(gemv_gateup_kernel<N>, g1, dim3(256), 0, st, x, s.d, s.f, s.k, s.E, \
-                                    w.gate_q, w.gate_s, w.up_q, w.up_s, idx, h32)
-  // d <= 8192: at most 4 blocks per lane
-  if (nbl <= 1) K3_GU(1);
-  else if (nbl <= 2) K3_GU(2);
-  else K3_GU(4);
-#undef K3_GU
+  dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
+  hipLaunchKernelGGL(gemv_gateup_kernel, g1, dim3(256), 0, st, x, s.d, s.f, s.k, s.E, w.gate_q,
+                     w.gate_s, w.up_q, w.up_s, idx, h32);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const int nbfl = (s.f / 32 + 63) / 64;
-  dim3 g2(T, (s.d + kDownRowsPerBlock - 1) / kDownRowsPerBlock);
-#define K3_DN(N) hipLaunchKernelGGL(gemv_down_kernel<N>, g2, dim3(256), 0, st, s.d, s.f, s.k, s.E, \
-                                    w.down_q, w.down_s, idx, gate, h32, y)
-  // f <= 4096: at most 2 blocks per lane
-  if (nbfl <= 1) K3_DN(1);
-  else K3_DN(2);
-#undef K3_DN
+  dim3 g2(T, s.d / 16);
+  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(256), 0, st, s.d, s.f, s.k, s.E, w.down_q,
+                     w.down_s, idx, gate, h32, y);
   return hipGetLastError();
 }
 

@@ -5,10 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cstddef>
+
 namespace k3 {
 
 // Prefill grouped GEMM tile: tokens (sorted pairs) per tile.
-constexpr int kTileM = 64;
+constexpr int kTileM = 128;
 // Pairs per block of the grouping step.
 constexpr int kGroupChunk = 256;
 // Largest T served by the GEMV (decode) expert path.
@@ -24,9 +27,17 @@ struct ExpertWeights {
   const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
 };
 
+// layout.hip
+size_t tiled_scale_bytes(int n, int R, int K);
+hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int n, int R, int K,
+                       uint8_t* tcodes, uint8_t* tscales, hipStream_t st);
+
 // router_topk.hip
 hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const float* wr,
-                                const float* bias, float* logits, hipStream_t st);
+                                const uint16_t* wr3, const float* bias, float* logits,
+                                hipStream_t st);
+// three-term bf16 split of the router weights, w3 = [hi | mid | lo] each [E][d]
+hipError_t launch_router_split(const float* wr, int E, int d, uint16_t* w3, hipStream_t st);
 hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,
                        hipStream_t st);
 
@@ -44,14 +55,15 @@ hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const
 // gemm.hip (prefill path)
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,
                           hipStream_t st);
-hipError_t launch_clear_y(float* y, int T, int d, hipStream_t st);
 hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, const uint8_t* xq,
                               const uint8_t* xs, const int32_t* offsets, const int32_t* perm,
                               const int32_t* tiles, const int32_t* ntiles, int max_tiles,
                               uint8_t* hq, uint8_t* hs, hipStream_t st);
-hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const float* gate,
-                            const int32_t* offsets, const int32_t* perm, const int32_t* tiles,
-                            const int32_t* ntiles, int max_tiles, const uint8_t* hq,
-                            const uint8_t* hs, float* y, hipStream_t st);
+hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* offsets,
+                            const int32_t* perm, const int32_t* tiles, const int32_t* ntiles,
+                            int max_tiles, const uint8_t* hq, const uint8_t* hs, float* slots,
+                            hipStream_t st);
+hipError_t launch_combine(const float* slots, const int32_t* idx, const float* gate, int T,
+                          const Shape& s, float* y, hipStream_t st);
 
 }  // namespace k3

@@ -27,7 +27,8 @@ inline bool aligned(const void* p, size_t a) {
 
 // Byte offsets of every workspace buffer for one config.
 struct Plan {
-  size_t logits, idx, gate, counts, offsets, perm, bhist, tiles, ntiles, xq, xs, hq, hs, h32;
+  size_t logits, idx, gate, counts, offsets, perm, bhist, tiles, ntiles, xq, xs, hq, hs, h32,
+      slots, wr3;
   size_t total;
   int max_tiles;
 };
@@ -75,6 +76,8 @@ Plan make_plan(const k3moe_config* c) {
   p.hq = take(2 * P * f);
   p.hs = take(2 * P * (f / 32));
   p.h32 = take(tg * k * f * 4);
+  p.slots = take(P * d * 4);
+  p.wr3 = take(3 * E * d * 2);
   p.total = o;
   p.max_tiles = (int)tiles;
   return p;
@@ -116,6 +119,8 @@ struct k3moe {
   uint8_t* hq;
   uint8_t* hs;
   float* h32;
+  float* slots;
+  uint16_t* wr3;  // router weights as three bf16 terms, derived at create
   // stage timing (k3moe_profile_begin / k3moe_profile_end)
   bool prof_on;
   int prof_cap;
@@ -168,7 +173,7 @@ int run_router(k3moe* h, const uint16_t* x, int T, float* logits, int32_t* idx, 
                hipStream_t st) {
   const Shape s = shape_of(h);
   hipError_t e = stage(h, K3MOE_STAGE_ROUTER_LOGITS, st, [&] {
-    return k3::launch_router_logits(x, T, s, h->w.router_w, h->w.router_b, logits, st);
+    return k3::launch_router_logits(x, T, s, h->w.router_w, h->wr3, h->w.router_b, logits, st);
   });
   if (e != hipSuccess) return K3MOE_EHIP;
   e = stage(h, K3MOE_STAGE_TOPK, st, [&] { return k3::launch_topk(logits, T, s, idx, gate, st); });
@@ -204,12 +209,13 @@ int run_experts(k3moe* h, const uint16_t* x, int T, const int32_t* idx, const fl
                                   h->ntiles, max_tiles, h->hq, h->hs, st);
   });
   if (e != hipSuccess) return K3MOE_EHIP;
-  e = stage(h, K3MOE_STAGE_CLEAR_Y, st, [&] { return k3::launch_clear_y(y, T, s.d, st); });
-  if (e != hipSuccess) return K3MOE_EHIP;
   e = stage(h, K3MOE_STAGE_DOWN, st, [&] {
-    return k3::launch_gemm_down(T, s, w, gate, h->offsets, h->perm, h->tiles, h->ntiles,
-                                max_tiles, h->hq, h->hs, y, st);
+    return k3::launch_gemm_down(T, s, w, h->offsets, h->perm, h->tiles, h->ntiles, max_tiles,
+                                h->hq, h->hs, h->slots, st);
   });
+  if (e != hipSuccess) return K3MOE_EHIP;
+  e = stage(h, K3MOE_STAGE_COMBINE, st,
+            [&] { return k3::launch_combine(h->slots, idx, gate, T, s, y, st); });
   return hip_status(e);
 }
 
@@ -232,6 +238,22 @@ const char* k3moe_status_str(int status) {
     case K3MOE_EUNSUPPORTED: return "configuration not supported by this build";
     default: return "unknown status";
   }
+}
+
+int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K) {
+  if (n <= 0 || R <= 0 || K <= 0 || R % 16 != 0 || K % 128 != 0) return 0;
+  return (int64_t)k3::tiled_scale_bytes(n, R, K);
+}
+
+int k3moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t R, int32_t K,
+                     uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+  if (!codes || !scales || !tiled_codes || !tiled_scales) return K3MOE_EINVAL;
+  if (n <= 0 || R <= 0 || K <= 0 || R % 16 != 0 || K % 128 != 0) return K3MOE_EINVAL;
+  const void* ps[] = {codes, scales, tiled_codes, tiled_scales};
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return K3MOE_EINVAL;
+  return hip_status(k3::launch_pack(codes, scales, n, R, K, tiled_codes, tiled_scales,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 int64_t k3moe_workspace_bytes(const k3moe_config* cfg) {
@@ -285,6 +307,16 @@ int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3
   h->hq = h->ws + plan.hq;
   h->hs = h->ws + plan.hs;
   h->h32 = reinterpret_cast<float*>(h->ws + plan.h32);
+  h->slots = reinterpret_cast<float*>(h->ws + plan.slots);
+  h->wr3 = reinterpret_cast<uint16_t*>(h->ws + plan.wr3);
+  if (k3::launch_router_split(w->router_w, cfg->n_experts, cfg->d_model, h->wr3, nullptr) !=
+          hipSuccess ||
+      hipStreamSynchronize(nullptr) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(h->ws);
+    delete h;
+    return K3MOE_EHIP;
+  }
   *out = h;
   return K3MOE_OK;
 }

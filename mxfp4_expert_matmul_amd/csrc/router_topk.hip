@@ -7,6 +7,8 @@
 #include "k3_device.h"
 #include "k3_kernels.h"
 
+#include <algorithm>
+
 namespace k3 {
 
 // ---------------------------------------------------------------- logits, small T
@@ -64,56 +66,89 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- logits, large T
-// Tiled fp32 GEMM: 64 tokens x 64 experts per workgroup, K staged in LDS in
-// steps of 32; each thread owns a 4x4 block of outputs.
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x, int T,
-                                                          int d, const float* __restrict__ wr,
+// The fp32 router weights are split once (at handle creation) into three bf16
+// terms w = hi + mid + lo, which is exact (24 significant bits = 3 x 8). x is
+// bf16, so every product x * term is exact in fp32 and the logits come from
+// bf16 MFMAs (v_mfma_f32_16x16x32_bf16) accumulating in fp32: the same
+// arithmetic class as an fp32 dot product, at MFMA rate.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, size_t n,
+                                                           uint16_t* __restrict__ w3) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const float w = wr[i];
+    const uint16_t hi = f32_to_bf16_rne(w);
+    const float r1 = w - bf16_bits_to_f32(hi);
+    const uint16_t mid = f32_to_bf16_rne(r1);
+    const float r2 = r1 - bf16_bits_to_f32(mid);
+    w3[i] = hi;
+    w3[n + i] = mid;
+    w3[2 * n + i] = f32_to_bf16_rne(r2);
+  }
+}
+
+// grid: (ceil(T / 64), ceil(E / 64)), block 256. Wave w owns experts
+// e0 + 16 w .. +15 (MFMA rows) for tokens t0 .. t0 + 63 (four 16-column tiles).
+// MFMA operand lane l: row/column l % 16, 8 consecutive K at 8 (l / 16); both
+// operands use the same layout, so any consistent K order is a valid sum.
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x, int T,
+                                                          int d, const uint16_t* __restrict__ w3,
                                                           const float* __restrict__ bias, int E,
                                                           float* __restrict__ logits) {
-  __shared__ float xs[32][64 + 4];  // [k][token]
-  __shared__ float ws[32][64 + 4];  // [k][expert]
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tr = (tid >> 4) * 4;  // token offset in tile
-  const int er = (tid & 15) * 4;  // expert offset in tile
-  float acc[4][4] = {};
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64 + 16 * wave;
+  const size_t n = (size_t)E * d;
+  const int ea = min(e0 + r, E - 1);
+  const uint16_t* ap = w3 + (size_t)ea * d + 8 * g;
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) bp[ct] = x + (size_t)min(t0 + 16 * ct + r, T - 1) * d + 8 * g;
+  v4f acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
   for (int k0 = 0; k0 < d; k0 += 32) {
-    // load 64x32 of x (bf16) and 64x32 of wr: 2048 elements each, 8 per thread
+    v8bf a[3], b[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int li = tid + 256 * r;  // 0..2047
-      int row = li >> 5, kk = li & 31;
-      int t = t0 + row, e = e0 + row;
-      xs[kk][row] = (t < T) ? bf16_bits_to_f32(x[(size_t)t * d + k0 + kk]) : 0.0f;
-      ws[kk][row] = (e < E) ? wr[(size_t)e * d + k0 + kk] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float a[4], b[4];
+    for (int q = 0; q < 3; ++q) a[q] = *reinterpret_cast<const v8bf*>(ap + q * n + k0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[kk][tr + i]; b[i] = ws[kk][er + i]; }
+    for (int ct = 0; ct < 4; ++ct) b[ct] = *reinterpret_cast<const v8bf*>(bp[ct] + k0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
+      for (int q = 0; q < 3; ++q)
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b[ct], acc[ct], 0, 0, 0);
   }
+  // result element i of lane l: expert e0 + 4 g + i, token t0 + 16 ct + r
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int t = t0 + tr + i;
+  for (int ct = 0; ct < 4; ++ct) {
+    const int t = t0 + 16 * ct + r;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = e0 + er + j;
-      if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * g + i;
+      if (e < E) logits[(size_t)t * E + e] = acc[ct][i] + (bias ? bias[e] : 0.0f);
     }
   }
 }
 
+hipError_t launch_router_split(const float* wr, int E, int d, uint16_t* w3, hipStream_t st) {
+  const size_t n = (size_t)E * d;
+  hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 8192)),
+                     dim3(256), 0, st, wr, n, w3);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const float* wr,
-                                const float* bias, float* logits, hipStream_t st) {
+                                const uint16_t* wr3, const float* bias, float* logits,
+                                hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (T <= kRouterGemvMaxT) {
     dim3 grid(s.E);
@@ -125,7 +160,7 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
       hipLaunchKernelGGL(router_gemv_kernel<8>, grid, dim3(256), 0, st, x, T, s.d, wr, bias, s.E, logits);
   } else {
     dim3 grid((T + 63) / 64, (s.E + 63) / 64);
-    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, st, x, T, s.d, wr, bias, s.E, logits);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, st, x, T, s.d, wr3, bias, s.E, logits);
   }
   return hipGetLastError();
 }
@@ -137,6 +172,32 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
 // as -inf so a valid index is always chosen.
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
+}
+
+// One DPP step of the arg-max reduction: combine with the lane selected by
+// CTRL (row_mask selects the 16-lane rows that take part; others keep their
+// own pair).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Arg-max over the 64 lanes in the order (value descending, index ascending):
+// quad swaps, half-row and row mirrors give every lane its 16-lane row's best;
+// row broadcasts of lanes 15 and 31 carry the rows forward so lane 63 holds
+// the wave's best, which is then read by every lane.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1, 0xf>(v, i);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E, 0xf>(v, i);   // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xf>(v, i);  // row_half_mirror
+  argmax_step<0x140, 0xf>(v, i);  // row_mirror
+  argmax_step<0x142, 0xa>(v, i);  // row_bcast15 into rows 1 and 3
+  argmax_step<0x143, 0xc>(v, i);  // row_bcast31 into rows 2 and 3
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 template <int V>  // logits per lane: E <= 64 * V
@@ -167,12 +228,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       const bool below = (v[j] < pv) || (v[j] == pv && e > pi);
       if (e < E && below && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_argmax(bv, bi);  // every lane gets the wave's best (value, index)
     pv = bv;
     pi = bi;
     if (lane == r) myv = bv;

@@ -27,23 +27,42 @@ def _load():
         for fn in (lib.k3synth_fill_codes, lib.k3synth_fill_scales):
             fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
             fn.restype = ctypes.c_int
+        for fn in (lib.k3synth_fill_codes_tiled, lib.k3synth_fill_scales_tiled):
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_uint64, ctypes.c_void_p]
+            fn.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
-def device_weights(cfg: LayerConfig, device="cuda:0") -> dict:
+def tiled_scale_bytes(n: int, R: int, K: int) -> int:
+    """Bytes of scales for n stacked R x K matrices in the tiled layout."""
+    return n * (R // 16) * ((K // 128 + 3) // 4) * 256
+
+
+def device_weights(cfg: LayerConfig, device="cuda:0", tiled: bool = True) -> dict:
     """All layer weights on the device: router_w, router_b (or None) and the
-    six MXFP4 tensors (uint8), generated in place."""
+    six MXFP4 tensors (uint8, flat), generated in place. With tiled=True the
+    codes and scales are in the tiled layout the layer library reads (the
+    same draws, placed by their row-major index); else row-major."""
     import torch
     lib = _load()
     dev = torch.device(device)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    dims = {"gate": (cfg.f, cfg.d), "up": (cfg.f, cfg.d), "down": (cfg.d, cfg.f)}
     out = {}
     for name, shape in cfg.tensor_shapes().items():
-        t = torch.empty(shape, dtype=torch.uint8, device=dev)
         key = stream_key(cfg.seed, WEIGHT_STREAMS[name])
-        fn = lib.k3synth_fill_codes if name.endswith("_q") else lib.k3synth_fill_scales
-        rc = fn(ctypes.c_void_p(t.data_ptr()), t.numel(), key, stream)
+        R, K = dims[name[:-2]]
+        if tiled:
+            nbytes = int(np.prod(shape)) if name.endswith("_q") else tiled_scale_bytes(cfg.E, R, K)
+            t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            fn = lib.k3synth_fill_codes_tiled if name.endswith("_q") else lib.k3synth_fill_scales_tiled
+            rc = fn(ctypes.c_void_p(t.data_ptr()), cfg.E, R, K, key, stream)
+        else:
+            t = torch.empty(shape, dtype=torch.uint8, device=dev)
+            fn = lib.k3synth_fill_codes if name.endswith("_q") else lib.k3synth_fill_scales
+            rc = fn(ctypes.c_void_p(t.data_ptr()), t.numel(), key, stream)
         if rc != 0:
             raise RuntimeError(f"synth fill of {name} failed ({rc})")
         out[name] = t
@@ -62,6 +81,7 @@ def device_x(cfg: LayerConfig, T: int | None = None, start_token: int = 0, strea
 
 
 def host_weights_to_device(w: dict, router_w: np.ndarray, bias, device="cuda:0") -> dict:
+    """Row-major host weights copied to the device as they are."""
     import torch
     out = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in w.items()}
     out["router_w"] = torch.from_numpy(np.ascontiguousarray(router_w)).to(device)

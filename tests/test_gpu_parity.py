@@ -39,13 +39,15 @@ class Small:
     """A small layer fully resident on host (oracle) and device."""
 
     def __init__(self, cfg, max_tokens):
+        import mxfp4_expert_matmul_amd as k3m
         from synth.device import host_weights_to_device
         self.cfg = cfg
         self.W = synth.gen_weights(cfg)
         self.wr = synth.gen_router_w(cfg)
         self.bias = synth.gen_bias(cfg)
         self.src = synth.ExpertSource(cfg, self.W)
-        self.dw = host_weights_to_device(self.W, self.wr, self.bias)
+        rowmajor = host_weights_to_device(self.W, self.wr, self.bias)
+        self.dw = k3m.pack_layer_weights(rowmajor, cfg.E, cfg.d, cfg.f)
 
 
 def _layer(k3, cfg, dw, max_tokens):
@@ -87,14 +89,48 @@ def _run_and_check(k3, layer, cfg, x_bits, src, wr, bias, tokens=None, label="")
 
 # ----------------------------------------------------------------- generator
 
+def _tiled_reference(codes, scales, R, K):
+    """The tiled layout written out from its definition in k3moe.h (numpy)."""
+    n = codes.shape[0]
+    RT, KT = R // 16, K // 128
+    KG = (KT + 3) // 4
+    tc = np.zeros((n, RT, KT, 64, 16), dtype=np.uint8)
+    ts = np.full((n, RT, KG, 64, 4), 127, dtype=np.uint8)
+    for lane in range(64):
+        r, g = lane % 16, lane // 16
+        for rt in range(RT):
+            row = 16 * rt + r
+            for kt in range(KT):
+                tc[:, rt, kt, lane, :] = codes[:, row, 64 * kt + 16 * g: 64 * kt + 16 * g + 16]
+                ts[:, rt, kt // 4, lane, kt % 4] = scales[:, row, 4 * kt + g]
+    return tc.reshape(-1), ts.reshape(-1)
+
+
+def test_pack_matches_layout_definition(k3):
+    rng = np.random.default_rng(5)
+    for n, R, K in [(2, 32, 128), (1, 48, 640), (3, 16, 512)]:
+        codes = rng.integers(0, 256, (n, R, K // 2), dtype=np.uint8)
+        scales = rng.integers(0, 256, (n, R, K // 32), dtype=np.uint8)
+        tc, ts = k3.pack_mxfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), n, R, K)
+        torch.cuda.synchronize()
+        wc, ws = _tiled_reference(codes, scales, R, K)
+        assert np.array_equal(tc.cpu().numpy(), wc), (n, R, K)
+        assert np.array_equal(ts.cpu().numpy(), ws), (n, R, K)
+
+
 def test_device_generator_matches_host(k3):
-    from synth.device import device_weights
+    from synth.device import device_weights, host_weights_to_device
     cfg = synth.CONFIGS[1]
-    dw = device_weights(cfg)
     W = synth.gen_weights(cfg)
+    rowmajor = device_weights(cfg, tiled=False)
     for name, arr in W.items():
-        assert np.array_equal(dw[name].cpu().numpy(), arr), name
-    assert np.array_equal(dw["router_w"].cpu().numpy(), synth.gen_router_w(cfg))
+        assert np.array_equal(rowmajor[name].cpu().numpy(), arr), name
+    assert np.array_equal(rowmajor["router_w"].cpu().numpy(), synth.gen_router_w(cfg))
+    tiled = device_weights(cfg)
+    packed = k3.pack_layer_weights(host_weights_to_device(W, synth.gen_router_w(cfg), None),
+                                   cfg.E, cfg.d, cfg.f)
+    for name in W:
+        assert np.array_equal(tiled[name].cpu().numpy(), packed[name].cpu().numpy()), name
 
 
 # ----------------------------------------------------------------- small layers
