@@ -253,12 +253,15 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
             ws.q[m][rt][s] = *reinterpret_cast<const uint4*>(
                 wq_t[m] + ((size_t)rt * KT + kChunkTiles * c + s) * 1024);
   };
-  int sw[NM][NRT];  // scale dwords of the current group of 4 K tiles
-  auto s_load = [&](int kg) {
+  // scale dwords of the current group of 4 K tiles (sw) and of the next
+  // (swn), loaded one iteration ahead so the MFMAs never wait on a load that
+  // was issued behind direct-to-LDS copies
+  int sw[NM][NRT], swn[NM][NRT];
+  auto s_load = [&](int kg, int (&dst)[NM][NRT]) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) sw[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
+      for (int rt = 0; rt < NRT; ++rt) dst[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
   };
 
   // ---- activations: wave instruction j = 8 wave + i (64 per chunk): term
@@ -354,10 +357,12 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
   auto tiles_of = [&](int c) { return min(kChunkTiles, KT - kChunkTiles * c); };
   WStage wa, wb;
   act_issue(lds0, 0, tiles_of(0));
-  if (wave_on) w_load(0, tiles_of(0), wa);
+  if (wave_on) {
+    w_load(0, tiles_of(0), wa);
+    s_load(0, sw);
+  }
   __syncthreads();  // also waits for this thread's direct-to-LDS loads
   for (int c = 0; c < nchunks; c += 2) {
-    if (wave_on) s_load(c >> 1);
     {  // even chunk c: buffer 0, weights wa, scale bytes 0/1
       const bool more = (c + 1) < nchunks;
       if (more) {
@@ -372,10 +377,17 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
       const bool more = (c + 2) < nchunks;
       if (more) {
         act_issue(lds0, c + 2, tiles_of(c + 2));
-        if (wave_on) w_load(c + 2, tiles_of(c + 2), wa);
+        if (wave_on) {
+          w_load(c + 2, tiles_of(c + 2), wa);
+          s_load((c + 2) >> 1, swn);
+        }
       }
       if (wave_on) compute(lds1, tiles_of(c + 1), wb, 2);
       __syncthreads();
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) sw[m][rt] = swn[m][rt];
     }
   }
   if (!wave_on) return;
