@@ -119,14 +119,15 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c)
 }
 
 // ------------------------------------------------------------- grouped GEMM
-// One workgroup = 8 waves = one (tile, row block): up to kTileM tokens of one
-// expert (a tile of the grouped pairs) times a block of weight rows.
+// One workgroup = 4 waves = one (tile, row block): up to kTileM = 64 tokens
+// of one expert (a tile of the grouped pairs) times a block of weight rows.
 //   gate/up (kGateUp): 128 features = 128 gate rows + the same 128 up rows;
 //   down    (kDown):   256 output rows.
-// Waves are laid out 4 (along rows) x 2 (along tokens): wave (nw, mw) owns 32
-// features (gate/up: two 16-row MFMA tiles of gate and the same two of up, so
-// SwiGLU pairs sit in one lane) or 64 rows (down: four 16-row tiles), for the
-// 64 tokens 64 mw .. 64 mw + 63 (four 16-column MFMA tiles).
+// Wave w owns 32 features (gate/up: two 16-row MFMA tiles of gate and the
+// same two of up, so SwiGLU pairs sit in one lane) or 64 rows (down: four
+// 16-row tiles), for all 64 tokens of the tile (four 16-column MFMA tiles).
+// Two workgroups share a CU, so one computes while the other waits for
+// memory.
 //
 // Weights (tiled layout, layout.hip) go straight to registers: one MFMA A
 // operand is one 1 KB tile, read with one coalesced 16-byte-per-lane load,
@@ -143,7 +144,7 @@ constexpr int kDown = 1;
 constexpr int kChunkTiles = 2;                  // K tiles (128 columns) per chunk
 constexpr int kActRow = kChunkTiles * 128;      // LDS bytes per token row and term
 constexpr int kScRow = kChunkTiles * 4;         // LDS scale bytes per token row and term
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 
 template <int MODE>
 struct GemmShape {
@@ -158,14 +159,19 @@ struct TileInfo {
 };
 
 // Workgroup -> (tile, row block). Workgroups are dispatched round-robin over
-// the 8 XCDs; consecutive workgroups of one XCD take consecutive row blocks
-// of the same tile, so a tile's activations are fetched into that XCD's L2
-// once and its row blocks run together.
-__device__ __forceinline__ void block_coords(int nrb, int& tile, int& rb) {
+// the 8 XCDs. Each XCD takes a contiguous range of the tile list (the tiles
+// of one expert are adjacent in it) and walks it tile by tile, all row blocks
+// of a tile back to back: a tile's activations are fetched into that XCD's
+// L2 once, and consecutive tiles of one expert find its weights in the
+// XCD's L2 or the memory-side cache. (Interleaving the row blocks of two
+// tiles measured slower.)
+__device__ __forceinline__ void block_coords(int nrb, int ntiles, int& tile, int& rb) {
   const int lid = blockIdx.x;
   const int xcd = lid & 7, q = lid >> 3;
-  tile = (q / nrb) * 8 + xcd;
+  const int tpx = (ntiles + 7) / 8;  // tiles per XCD
+  const int lt = q / nrb;            // tile within the XCD's range
   rb = q % nrb;
+  tile = (lt < tpx) ? xcd * tpx + lt : ntiles;  // ntiles = no work
 }
 
 __device__ __forceinline__ bool load_tile(int tile, const int32_t* tiles, const int32_t* ntiles,
@@ -187,7 +193,7 @@ struct ActLds {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
+__global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     int K, int nrows, int f_out, int k, const uint8_t* __restrict__ wq0,
     const uint8_t* __restrict__ ws0, const uint8_t* __restrict__ wq1,
     const uint8_t* __restrict__ ws1, const uint8_t* __restrict__ act_hi,
@@ -207,17 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
   __shared__ int tok_lds[kTileM];
 
   int tile, rb;
-  block_coords(nrb, tile, rb);
+  block_coords(nrb, ntiles[0], tile, rb);
   TileInfo ti;
   if (!load_tile(tile, tiles, ntiles, offsets, ti)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int nw = wave & 3, mw = wave >> 2;
+  const int nw = wave;
   const int r = lane & 15, g = lane >> 4;
   const int nb = K >> 5, KT = K >> 7, KG = (KT + 3) >> 2, RT = nrows >> 4;
   const int row_base = rb * G::kRowsPerBlock;          // first output row of the block
   const int w0 = row_base + nw * G::kRowsPerWave;       // first output row of this wave
-  const int m0 = 64 * mw;                               // first tile token of this wave
+  const int m0 = 0;                                     // first tile token of this wave
   const int nct = max(0, min(NCT, (ti.cnt - m0 + 15) >> 4));  // token tiles of this wave
   const bool wave_on = (w0 < nrows) && (nct > 0);
 
@@ -264,26 +270,26 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
       for (int rt = 0; rt < NRT; ++rt) dst[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
   };
 
-  // ---- activations: wave instruction j = 8 wave + i (64 per chunk): term
-  // j / 32, token rows 4 (j % 32) .. +3; lane -> row + lane / 16, slot lane % 16
+  // ---- activations: wave instruction j = 8 wave + i (32 per chunk): term
+  // j / 16, token rows 4 (j % 16) .. +3; lane -> row + lane / 16, slot lane % 16
   // holding piece slot ^ (row % 16). Scales: one 4-byte copy per lane, wave w
-  // -> term w / 4, rows 32 (w % 4) + lane / 2, half lane % 2.
-  const uint8_t* act_t = (wave < 4) ? act_hi : act_lo;
+  // -> term w / 2, rows 32 (w % 2) + lane / 2, half lane % 2.
+  const uint8_t* act_t = (wave < 2) ? act_hi : act_lo;
   uint32_t asrc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = 8 * wave + i;
-    const int row = 4 * (j & 31) + (lane >> 4);
+    const int row = 4 * (j & 15) + (lane >> 4);
     asrc[i] = (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 15) ^ (row & 15));
   }
-  const int sc_row = 32 * (wave & 3) + (lane >> 1);
-  const uint8_t* sc_src = ((wave < 4) ? acts_hi : acts_lo) + (size_t)tok_lds[sc_row] * nb;
+  const int sc_row = 32 * (wave & 1) + (lane >> 1);
+  const uint8_t* sc_src = ((wave < 2) ? acts_hi : acts_lo) + (size_t)tok_lds[sc_row] * nb;
   auto act_issue = [&](ActLds& L, int c, int S) {
     const uint32_t kb = (uint32_t)(kChunkTiles * c) * 128u;  // first column of the chunk
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = 8 * wave + i;
-      const int term = j >> 5, row0 = 4 * (j & 31);
+      const int term = j >> 4, row0 = 4 * (j & 15);
       if (row0 < ti.cnt) {
         uint32_t off = asrc[i] + kb;
         if (S < kChunkTiles) off -= 16u * (((lane & 15) ^ ((row0 + (lane >> 4)) & 15)) & 8u);
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void mx_gemm_kernel(
     {
       const int half = (S < kChunkTiles) ? 0 : (lane & 1);
       __builtin_amdgcn_global_load_lds(sc_src + (kb >> 5) + 4 * half,
-                                       (lds_ptr)&L.s[wave >> 2][32 * (wave & 3)][0], 4, 0, 0);
+                                       (lds_ptr)&L.s[wave >> 1][32 * (wave & 1)][0], 4, 0, 0);
     }
   };
 
@@ -487,8 +493,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   reinterpret_cast<float4*>(y)[i] = acc;
 }
 
+// 8 XCDs x tiles per XCD x row blocks; the kernel sees the actual tile count
+// and idles workgroups beyond it
 static unsigned gemm_grid(int max_tiles, int nrb) {
-  return (unsigned)(((max_tiles + 7) / 8) * 8 * nrb);
+  return (unsigned)(8 * ((max_tiles + 7) / 8) * nrb);
 }
 
 hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, const uint8_t* xq,
