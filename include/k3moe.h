@@ -59,10 +59,14 @@ extern "C" {
 typedef struct k3moe k3moe;  /* opaque handle */
 
 /* Layer shape (HOST struct, copied by k3moe_create).
- * Supported: d % 128 == 0 and 128 <= d <= 16384; f % 128 == 0 and
- * 128 <= f <= 16384; 1 <= k <= E <= 4096; k <= 64; 1 <= max_tokens and
- * max_tokens * k < 2^31. Anything else returns K3MOE_EINVAL (malformed) or
- * K3MOE_EUNSUPPORTED (well-formed but beyond these limits). */
+ * Supported: d % 128 == 0 and 128 <= d <= 8192; f % 128 == 0 and
+ * 128 <= f <= 4096; 1 <= k <= E <= 4096; k <= 64; 1 <= max_tokens,
+ * max_tokens * k < 2^31, max_tokens * d <= 2^30 and max_tokens * k * f <= 2^30
+ * (32-bit offsets into the prefill activation planes; at d=7168, k=16,
+ * f=2048 that is up to 32768 tokens per call). Anything else returns
+ * K3MOE_EINVAL (malformed: non-positive sizes, d or f not a multiple of 32,
+ * k > E, flags != 0) or K3MOE_EUNSUPPORTED (well-formed but beyond these
+ * limits). */
 typedef struct {
   int32_t d_model;     /* d: hidden size */
   int32_t n_experts;   /* E: routed experts */

@@ -121,67 +121,125 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 }
 
 // down + combine: workgroup = one token x one 16-row tile of the output; its
-// 4 waves split the token's k slots (wave w: j = w, w+4, ...). Lane (r, g)
+// 4 waves split the token's k slots (wave w: j = w, w + 4, ...). For each
+// slot a wave issues the loads of all its K tiles (the next slot's are issued
+// before the current one is computed), stages the pair's h (fp32) in its own
+// LDS region and reads each 32-value block of it as a broadcast. Lane (r, g)
 // keeps a gate-weighted partial of row 16 rt + r over K block g of every
-// tile; partials meet across groups, then across waves in fixed order
-// through LDS. Deterministic, no atomics.
-// grid: (T, d / 16), block 256.
+// tile; partials meet across lane groups, then across waves in fixed order.
+// Deterministic, no atomics.
+// grid: (T, d / 16), block 256, dynamic LDS 16 f bytes.
+constexpr int kDownTiles = 8;  // K tiles per step (a slot of f = 2048 takes 2 steps)
 __global__ __launch_bounds__(256) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ h32, float* __restrict__ y) {
-  __shared__ float part[4][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) float hl[];  // [4][f]
+  __shared__ float red[4][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t = blockIdx.x, rt = blockIdx.y;
   const int RT = d >> 4, KT = f >> 7, KG = (KT + 3) >> 2;
-  float acc = 0.0f;
-  for (int j = wave; j < k; j += 4) {
-    const int pair = t * k + j;
-    const int e = idx[pair];
-    if (e < 0 || e >= E) continue;  // dropped pair contributes zero
-    const float gw = gate[pair];
+  float* hw = hl + (size_t)wave * f;
+  struct Slot {
+    uint4 q[kDownTiles];
+    uint32_t sw[kDownTiles / 4];
+  };
+  // loads of K tiles kt0 .. kt0 + 15 of slot j's expert (nothing for a
+  // dropped slot)
+  auto issue = [&](int j, int kt0, Slot& sl) {
+    const int e = idx[(size_t)t * k + j];
+    if (e < 0 || e >= E) return;
     const size_t tile0 = ((size_t)e * RT + rt) * KT;
     const uint8_t* qt = dq + tile0 * 1024 + 16 * lane;
     const uint32_t* st = reinterpret_cast<const uint32_t*>(ds + ((size_t)e * RT + rt) * KG * 256) + lane;
-    const float* ht = h32 + (size_t)pair * f + 32 * g;
+    const int n = min(kDownTiles, KT - kt0);
+#pragma unroll
+    for (int i = 0; i < kDownTiles; ++i)
+      if (i < n) sl.q[i] = *reinterpret_cast<const uint4*>(qt + (size_t)(kt0 + i) * 1024);
+#pragma unroll
+    for (int s2 = 0; s2 < kDownTiles / 4; ++s2)
+      if (4 * s2 < n) sl.sw[s2] = st[64 * ((kt0 >> 2) + s2)];
+  };
+  float acc = 0.0f;
+  // h of slot j: its first 2048 values go through registers (loaded before
+  // the next step's weights, so waiting for them does not wait for those),
+  // the rest (f > 2048) straight into LDS
+  constexpr int kStageF4 = 8;  // float4 per lane held in registers
+  const int n4 = f >> 2;
+  auto compute = [&](int j, int kt0, const Slot& sl) {
+    const int pair = t * k + j;
+    const int n = min(kDownTiles, KT - kt0);
     float pe = 0.0f;
-    for (int kg = 0; kg < KG; ++kg) {
-      const uint32_t sw = st[64 * kg];
-      const int nk = min(4, KT - 4 * kg);
 #pragma unroll
-      for (int j2 = 0; j2 < 4; j2 += 2) {
-        uint4 q[2];
-        float hv[2][32];
+    for (int i = 0; i < kDownTiles; ++i)
+      if (i < n) {
+        const float4* hs = reinterpret_cast<const float4*>(hw + 128 * (kt0 + i) + 32 * g);
+        float hv[32];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (j2 + u < nk) {
-            const int kt = 4 * kg + j2 + u;
-            q[u] = *reinterpret_cast<const uint4*>(qt + (size_t)kt * 1024);
-            const float4* hs = reinterpret_cast<const float4*>(ht + 128 * kt);
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              const float4 h4 = hs[v];
-              hv[u][4 * v] = h4.x; hv[u][4 * v + 1] = h4.y; hv[u][4 * v + 2] = h4.z; hv[u][4 * v + 3] = h4.w;
-            }
-          }
+        for (int v = 0; v < 8; ++v) {
+          const float4 h4 = hs[v];
+          hv[4 * v] = h4.x; hv[4 * v + 1] = h4.y; hv[4 * v + 2] = h4.z; hv[4 * v + 3] = h4.w;
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (j2 + u < nk)
-            pe = fmaf(block_dot_f32(q[u], hv[u]), e8m0_to_f32((sw >> (8 * (j2 + u))) & 0xffu), pe);
+        pe = fmaf(block_dot_f32(sl.q[i], hv),
+                  e8m0_to_f32((sl.sw[i >> 2] >> (8 * (i & 3))) & 0xffu), pe);
       }
+    acc = fmaf(gate[pair], pe, acc);
+  };
+  auto valid = [&](int j) {
+    const int e = idx[(size_t)t * k + j];
+    return e >= 0 && e < E;  // a dropped pair contributes zero
+  };
+  // the wave's (slot, 16-tile chunk) steps; step s+1's weights are issued
+  // after step s's h is loaded and before step s is computed
+  const int nchunk = (KT + kDownTiles - 1) / kDownTiles;
+  const int nslot = (k - wave + 3) / 4;  // slots wave, wave + 4, ...
+  const int nstep = nslot * nchunk;
+  Slot sa, sb;
+  auto step = [&](int s, Slot& cur, Slot& nxt) {
+    const int j = wave + 4 * (s / nchunk), kt0 = kDownTiles * (s % nchunk);
+    const bool on = valid(j);
+    const bool stage = on && kt0 == 0;
+    const float4* hsrc = reinterpret_cast<const float4*>(h32 + (size_t)(t * k + j) * f);
+    float4 hr0, hr1, hr2, hr3, hr4, hr5, hr6, hr7;  // lane + 64 v, v = 0..7 (clamped)
+    if (stage) {
+      hr0 = hsrc[min(lane, n4 - 1)];
+      hr1 = hsrc[min(lane + 64, n4 - 1)];
+      hr2 = hsrc[min(lane + 128, n4 - 1)];
+      hr3 = hsrc[min(lane + 192, n4 - 1)];
+      hr4 = hsrc[min(lane + 256, n4 - 1)];
+      hr5 = hsrc[min(lane + 320, n4 - 1)];
+      hr6 = hsrc[min(lane + 384, n4 - 1)];
+      hr7 = hsrc[min(lane + 448, n4 - 1)];
     }
-    acc = fmaf(gw, pe, acc);
+    if (s + 1 < nstep) issue(wave + 4 * ((s + 1) / nchunk), kDownTiles * ((s + 1) % nchunk), nxt);
+    if (!on) return;
+    if (stage) {
+      float4* hd = reinterpret_cast<float4*>(hw);
+      if (lane < n4) hd[lane] = hr0;
+      if (lane + 64 < n4) hd[lane + 64] = hr1;
+      if (lane + 128 < n4) hd[lane + 128] = hr2;
+      if (lane + 192 < n4) hd[lane + 192] = hr3;
+      if (lane + 256 < n4) hd[lane + 256] = hr4;
+      if (lane + 320 < n4) hd[lane + 320] = hr5;
+      if (lane + 384 < n4) hd[lane + 384] = hr6;
+      if (lane + 448 < n4) hd[lane + 448] = hr7;
+      for (int i = lane + 64 * kStageF4; i < n4; i += 64) hd[i] = hsrc[i];
+    }
+    compute(j, kt0, cur);
+  };
+  if (nstep > 0) issue(wave, 0, sa);
+  for (int s = 0; s < nstep; s += 2) {
+    step(s, sa, sb);
+    if (s + 1 < nstep) step(s + 1, sb, sa);
   }
   acc += __shfl_xor(acc, 16, 64);
   acc += __shfl_xor(acc, 32, 64);
-  if (g == 0) part[wave][r] = acc;
+  if (g == 0) red[wave][r] = acc;
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const float s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
-                    part[3][threadIdx.x];
-    y[(size_t)t * d + 16 * rt + threadIdx.x] = s;
+  if (tid < 16) {
+    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    y[(size_t)t * d + 16 * rt + tid] = s;
   }
 }
 
@@ -194,12 +252,17 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
   return hipGetLastError();
 }
 
+hipError_t prepare_gemv(const Shape& s) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 16 * s.f);
+}
+
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   dim3 g2(T, s.d / 16);
-  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(256), 0, st, s.d, s.f, s.k, s.E, w.down_q,
-                     w.down_s, idx, gate, h32, y);
+  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(256), (size_t)16 * s.f, st, s.d, s.f, s.k, s.E,
+                     w.down_q, w.down_s, idx, gate, h32, y);
   return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
                               const int32_t* idx, float* h32, hipStream_t st);
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st);
+// once per handle: raise the dynamic LDS limit the decode down kernel needs
+hipError_t prepare_gemv(const Shape& s);
 
 // gemm.hip (prefill path)
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,

@@ -45,6 +45,12 @@ int check_config(const k3moe_config* c) {
   if (c->d_model > 8192 || c->d_ff > 4096) return K3MOE_EUNSUPPORTED;
   if (c->n_experts > 4096 || c->top_k > 64) return K3MOE_EUNSUPPORTED;
   if ((int64_t)c->max_tokens * c->top_k >= (int64_t)1 << 31) return K3MOE_EUNSUPPORTED;
+  // the prefill kernels address one plane of the activation split (T x d) and
+  // of the h split (T*k x f) with 32-bit byte offsets, and use offsets from
+  // 2^31 - 2^16 up as "read nothing"
+  if ((int64_t)c->max_tokens * c->d_model > (int64_t)1 << 30 ||
+      (int64_t)c->max_tokens * c->top_k * c->d_ff > (int64_t)1 << 30)
+    return K3MOE_EUNSUPPORTED;
   return K3MOE_OK;
 }
 
@@ -309,7 +315,8 @@ int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3
   h->h32 = reinterpret_cast<float*>(h->ws + plan.h32);
   h->slots = reinterpret_cast<float*>(h->ws + plan.slots);
   h->wr3 = reinterpret_cast<uint16_t*>(h->ws + plan.wr3);
-  if (k3::launch_router_split(w->router_w, cfg->n_experts, cfg->d_model, h->wr3, nullptr) !=
+  if (k3::prepare_gemv(shape_of(h)) != hipSuccess ||
+      k3::launch_router_split(w->router_w, cfg->n_experts, cfg->d_model, h->wr3, nullptr) !=
           hipSuccess ||
       hipStreamSynchronize(nullptr) != hipSuccess) {
     (void)hipGetLastError();

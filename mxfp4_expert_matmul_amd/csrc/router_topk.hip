@@ -166,78 +166,147 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
 }
 
 // ---------------------------------------------------------------- top-k + gates
-// One wave per token; the token's logits are read once into registers. Round
-// r selects the best element strictly below the previous selection in the
-// order (value descending, index ascending), so no mask is needed; NaN ranks
-// as -inf so a valid index is always chosen.
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// One wave per token; the token's logits are read once into registers as
+// 64-bit keys that order (value descending, index ascending): the high word
+// is the logit's bits mapped to an order-preserving unsigned integer (NaN
+// ranks as -inf), the low word the inverted expert index, so equal logits
+// rank the lower index higher. Round r takes the largest key strictly below
+// the previous round's, so no mask is needed and every step is a compare and
+// select (no branches).
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  if (v != v) b = 0xff800000u;                      // NaN ranks as -inf
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // order-preserving map
+  return ((uint64_t)b << 32) | (uint32_t)(~(uint32_t)e);
 }
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t b = (uint32_t)(key >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+__device__ __forceinline__ int topk_key_index(uint64_t key) { return (int)~(uint32_t)key; }
 
-// One DPP step of the arg-max reduction: combine with the lane selected by
-// CTRL (row_mask selects the 16-lane rows that take part; others keep their
-// own pair).
+// One DPP step of the 64-bit max: combine with the lane selected by CTRL
+// (ROW_MASK selects the 16-lane rows that take part; others keep their own).
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
-      __float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
-  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+__device__ __forceinline__ void max_step(uint64_t& key) {
+  const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xf, false);
+  const uint64_t other = ((uint64_t)ohi << 32) | olo;
+  key = other > key ? other : key;
 }
 
-// Arg-max over the 64 lanes in the order (value descending, index ascending):
-// quad swaps, half-row and row mirrors give every lane its 16-lane row's best;
-// row broadcasts of lanes 15 and 31 carry the rows forward so lane 63 holds
-// the wave's best, which is then read by every lane.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<0xB1, 0xf>(v, i);   // quad_perm [1,0,3,2]
-  argmax_step<0x4E, 0xf>(v, i);   // quad_perm [2,3,0,1]
-  argmax_step<0x141, 0xf>(v, i);  // row_half_mirror
-  argmax_step<0x140, 0xf>(v, i);  // row_mirror
-  argmax_step<0x142, 0xa>(v, i);  // row_bcast15 into rows 1 and 3
-  argmax_step<0x143, 0xc>(v, i);  // row_bcast31 into rows 2 and 3
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+// Max over the 64 lanes: quad swaps, half-row and row mirrors give every
+// lane its 16-lane row's max; row broadcasts of lanes 15 and 31 carry the
+// rows forward so lane 63 holds the wave's max, which every lane then reads.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
+  max_step<0xB1, 0xf>(key);   // quad_perm [1,0,3,2]
+  max_step<0x4E, 0xf>(key);   // quad_perm [2,3,0,1]
+  max_step<0x141, 0xf>(key);  // row_half_mirror
+  max_step<0x140, 0xf>(key);  // row_mirror
+  max_step<0x142, 0xa>(key);  // row_bcast15 into rows 1 and 3
+  max_step<0x143, 0xc>(key);  // row_bcast31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Selection (top k keys in descending order) of one wave's V keys per lane.
+// The k-th largest of the 64 lane maxima is a lower bound tau of the k-th
+// largest key (k distinct keys reach it), so every selected key is >= tau.
+// Usually few keys pass; they are compacted into LDS and each one's rank
+// (the number of passing keys above it) is its position. If more than 64
+// pass, k rounds each take the largest key below the previous round's.
+// Lane r < k returns selection r.
+template <int V>
+__device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand, uint64_t* sel) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) m[j] = key[j];
+#pragma unroll
+  for (int w = 1; w < V; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < V; j += 2 * w) m[j] = m[j + w] > m[j] ? m[j + w] : m[j];
+  // bitonic sort of the lane maxima, descending across the wave
+  uint64_t v = m[0];
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, j);
+      const bool take_max = ((lane & j) == 0) == ((lane & size) == 0);
+      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  const uint64_t tau =
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), k - 1) << 32) |
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, k - 1);
+  // compact the keys >= tau (in lane order; their order does not matter)
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const bool pass = key[j] >= tau;
+    const uint64_t bal = __ballot(pass);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (pass && c + below < 64) cand[c + below] = key[j];
+    c += __builtin_popcountll(bal);
+  }
+  if (c <= 64) {
+    const uint64_t mine = lane < c ? cand[lane] : 0ull;
+    int rank = 0;
+    for (int i = 0; i < c; ++i) rank += cand[i] > mine ? 1 : 0;
+    if (lane < c && rank < k) sel[rank] = mine;
+    return lane < k ? sel[lane] : 0ull;
+  }
+  // many keys above tau: k rounds over all keys
+  uint64_t prev = ~0ull, mine = 0ull;
+  for (int r = 0; r < k; ++r) {
+    uint64_t q[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] = key[j] < prev ? key[j] : 0ull;
+#pragma unroll
+    for (int w = 1; w < V; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < V; j += 2 * w) q[j] = q[j + w] > q[j] ? q[j + w] : q[j];
+    const uint64_t best = wave_max_u64(q[0]);
+    prev = best;
+    if (lane == r) mine = best;
+  }
+  return mine;
 }
 
 template <int V>  // logits per lane: E <= 64 * V
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ uint64_t cand[4][64];
+  __shared__ uint64_t sel[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;  // waves work independently (wave-private LDS, no barrier)
   const float* row = logits + (size_t)t * E;
-  const float NEG_INF = -__builtin_huge_valf();
-  float v[V];
+  uint64_t key[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int e = lane + 64 * j;
-    float a = (e < E) ? row[e] : NEG_INF;
-    v[j] = (a != a) ? NEG_INF : a;  // NaN ranks as -inf
+    key[j] = (e < E) ? topk_key(row[e], e) : 0ull;  // 0 is below every real key
   }
-  float pv = __builtin_huge_valf();  // previous selection (value, index)
-  int pi = -1;
-  float myv = NEG_INF;  // lane r keeps the value of selection r
-  for (int r = 0; r < k; ++r) {
-    float bv = NEG_INF;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int e = lane + 64 * j;
-      const bool below = (v[j] < pv) || (v[j] == pv && e > pi);
-      if (e < E && below && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
-    }
-    wave_argmax(bv, bi);  // every lane gets the wave's best (value, index)
-    pv = bv;
-    pi = bi;
-    if (lane == r) myv = bv;
-    if (lane == 0) idx[(size_t)t * k + r] = bi;
-  }
-  const float vmax = __shfl(myv, 0, 64);
-  float w = (lane < k) ? expf(myv - vmax) : 0.0f;
+  const uint64_t mine = select_topk<V>(key, k, cand[wv], sel[wv]);
+  const float v = topk_key_value(mine);
+  const float vmax = __shfl(v, 0, 64);
+  const float w = (lane < k) ? expf(v - vmax) : 0.0f;
   const float sum = wave_sum(w);
-  if (lane < k) gate[(size_t)t * k + lane] = w / sum;
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = topk_key_index(mine);
+    gate[(size_t)t * k + lane] = w / sum;
+  }
 }
 
 hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,

@@ -48,6 +48,10 @@ def test_status_strings(lib):
     ((128, 8000, 2, 256, 1), -4),    # E beyond the supported range
     ((128, 8, 64, 256, 1), -1),      # k > E
     ((128, 64, 64, 256, 2 ** 26), -4),  # T*k overflows int32
+    ((8192, 8, 2, 256, 2 ** 17 + 1), -4),  # T*d plane beyond 2^30 bytes
+    ((128, 896, 16, 4096, 2 ** 14 + 1), -4),  # T*k*f plane beyond 2^30 bytes
+    ((7168, 896, 16, 2048, 32768), "ok"),  # largest K3 token count within both limits
+    ((7168, 896, 16, 2048, 32769), -4),
 ])
 def test_workspace_bytes_validation(lib, cfg, want):
     n = lib.k3moe_workspace_bytes(lib.Config(*cfg))

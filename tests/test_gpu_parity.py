@@ -186,6 +186,77 @@ def test_batch_invariance(k3):
     layer.close()
 
 
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_graph_replay_matches_eager(k3, T):
+    """Forwards captured in one HIP graph (each with its own input and output
+    buffers) and replayed three times, with eager forwards of the same layer
+    in between, give exactly the eager outputs on every replay (decode GEMV
+    path for T <= 4, grouped path above: both deterministic)."""
+    cfg = synth.CONFIGS[1]
+    s = Small(cfg, 64)
+    layer = _layer(k3, cfg, s.dw, 64)
+    xs = [_x_dev(synth.gen_x(cfg, T=T, stream=10 + i)) for i in range(3)]
+    outs = [(torch.empty((T, cfg.d), dtype=torch.float32, device="cuda"),
+             torch.empty((T, cfg.k), dtype=torch.int32, device="cuda"),
+             torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")) for _ in xs]
+    ref = []
+    for x, (y, i, g) in zip(xs, outs):
+        k3.k3moe_layer_forward(layer.handle, x, y, i, g)
+        torch.cuda.synchronize()
+        ref.append((y.clone(), i.clone(), g.clone()))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x, (y, i, g) in zip(xs, outs):
+            k3.k3moe_layer_forward(layer.handle, x, y, i, g)
+    other = _x_dev(synth.gen_x(cfg, T=5, stream=20))
+    for rep in range(3):
+        for y, i, g in outs:  # stale values must be overwritten by the replay
+            y.fill_(float("nan"))
+            i.fill_(-7)
+            g.fill_(float("nan"))
+        layer.forward(other)  # eager work on the same handle between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (y, i, g), (ry, ri, rg) in zip(outs, ref):
+            assert torch.equal(i, ri) and torch.equal(g, rg), f"replay {rep}: routing differs"
+            assert torch.equal(y, ry), f"replay {rep}: output differs"
+    del graph
+    layer.close()
+
+
+@pytest.mark.parametrize("pattern", ["lanes_first", "all_tied", "random"])
+def test_topk_selection_patterns(k3, pattern):
+    """Top-k with E = 896 under logit patterns that take each branch of the
+    selection: ranks concentrated in a few lanes of the 64-lane selection
+    (more than 64 keys above the lower bound: the round-by-round branch), all
+    logits tied (ties resolve to the lowest indices), and random. x = 0, so
+    the logits are exactly the router bias."""
+    from synth.device import host_weights_to_device
+    cfg = synth.LayerConfig("topk_patterns", 128, 896, 16, 128, 4, 11)
+    W = synth.gen_weights(cfg)
+    wr = synth.gen_router_w(cfg)
+    e = np.arange(cfg.E)
+    if pattern == "lanes_first":
+        # experts e = lane + 64 j rank by (lane, j): lanes 0, 1, ... hold the largest
+        bias = (-0.01 * ((e % 64) * 14 + e // 64)).astype(np.float32)
+    elif pattern == "all_tied":
+        bias = np.full(cfg.E, 0.5, dtype=np.float32)
+    else:
+        bias = np.random.default_rng(5).standard_normal(cfg.E).astype(np.float32)
+    dw = k3.pack_layer_weights(host_weights_to_device(W, wr, bias), cfg.E, cfg.d, cfg.f)
+    layer = _layer(k3, cfg, dw, 8)
+    x = np.zeros((cfg.T, cfg.d), dtype=np.uint16)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    k3.k3moe_route(layer.handle, _x_dev(x), idx, gate)
+    torch.cuda.synchronize()
+    ridx, rgate = oracle.topk_gates(oracle.router_logits(x, wr, bias), cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(gate.cpu().numpy() - rgate)) <= 1e-6
+    layer.close()
+
+
 def test_route_and_group_entry_points(k3):
     cfg = synth.CONFIGS[1]
     s = Small(cfg, 300)
