@@ -22,9 +22,12 @@
 //                bytes 16-31 = K slots 64+16g .. 64+16g+15
 //   scale operand of lane l: row/column r, K slots 32g .. 32g+31
 //   result: lane l, element i -> row 4g + i of A, column l % 16 of B
-// The physical 32-element block behind MFMA slot-block kappa of step s of a
-// super-step of S steps starting at block kb0 is kb0 + S*kappa + s, so one
-// lane's S blocks of weights are contiguous (one 16*S-byte run per row).
+// One MFMA step covers one 128-column K tile: the weight lane (r, g) holds
+// the tile's 32-column block g of row r, and the activation lane (r, g) the
+// 16-column pieces g and 4 + g of token r, so every K slot pairs the same
+// physical column on both sides.
+#include <type_traits>
+
 #include "k3_device.h"
 #include "k3_kernels.h"
 
@@ -119,31 +122,39 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c)
 }
 
 // ------------------------------------------------------------- grouped GEMM
-// One workgroup = 4 waves = one (tile, row block): up to kTileM = 64 tokens
+// One workgroup = 4 waves = one (tile, row block): up to kTileM = 128 tokens
 // of one expert (a tile of the grouped pairs) times a block of weight rows.
+// At the long-prefill shapes an expert holds 50-130 tokens, so a tile is
+// nearly always a whole expert and its weights are read from HBM once.
 //   gate/up (kGateUp): 128 features = 128 gate rows + the same 128 up rows;
 //   down    (kDown):   256 output rows.
 // Wave w owns 32 features (gate/up: two 16-row MFMA tiles of gate and the
 // same two of up, so SwiGLU pairs sit in one lane) or 64 rows (down: four
-// 16-row tiles), for all 64 tokens of the tile (four 16-column MFMA tiles).
-// Two workgroups share a CU, so one computes while the other waits for
-// memory.
+// 16-row tiles), for all 128 tokens of the tile (eight 16-column MFMA
+// tiles). No two loads of a workgroup read the same bytes: a request for a
+// line that is still in flight stalls the CU's load path.
 //
-// Weights (tiled layout, layout.hip) go straight to registers: one MFMA A
-// operand is one 1 KB tile, read with one coalesced 16-byte-per-lane load,
-// one chunk ahead of the MFMAs; a scale dword per lane covers 4 K tiles.
-// Activations (two E4M3 terms + scales) of the tile's tokens are copied once
-// per workgroup straight into LDS (global_load_lds, four 256-byte token rows
-// per wave instruction; piece p of token row t at slot p ^ (t % 16) so an
-// MFMA column group reads 16 distinct bank groups), double-buffered.
-// K is walked in chunks of two 128-column tiles (a last chunk of one tile
-// when K/128 is odd); MFMA step s of chunk c is K tile 2c + s, and MFMA
-// slot-block kappa is that tile's 32-column block kappa.
+// Two workgroups share a CU (66 KB of LDS and at most 256 registers per
+// lane each), so one computes while the other waits for memory. K is walked
+// one 128-column tile at a time through two stages, the next tile's loads
+// issued before the current tile's MFMAs:
+//  - weights (tiled layout, layout.hip) go straight to registers: one MFMA A
+//    operand is one 1 KB tile, one coalesced 16-byte-per-lane load; a scale
+//    dword per lane covers 4 K tiles and is fetched with the group's first;
+//  - activations (two E4M3 terms + scales) of the tile's tokens are copied
+//    once per workgroup straight into LDS (global_load_lds; 16-byte piece p
+//    of token row t at slot p ^ (t % 8), so the 16 lanes of an MFMA column
+//    group read distinct bank groups).
+// Every wave issues the same number of loads per stage, so a stage is known
+// complete by waiting on the wave's load counter down to the count issued
+// after it (s_waitcnt vmcnt(N)), followed by a plain workgroup barrier; the
+// loads of the next stages stay in flight across it (a __syncthreads would
+// wait for all of them).
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
-constexpr int kChunkTiles = 2;                  // K tiles (128 columns) per chunk
-constexpr int kActRow = kChunkTiles * 128;      // LDS bytes per token row and term
-constexpr int kScRow = kChunkTiles * 4;         // LDS scale bytes per token row and term
+constexpr int kStages = 2;                 // ring depth (LDS buffers, weight register sets)
+constexpr int kActRow = 128;               // LDS bytes per token row and term (one K tile)
+constexpr int kScRow = 4;                  // scale bytes per token row and term (4 blocks)
 constexpr int kThreads = 256;
 
 template <int MODE>
@@ -153,6 +164,60 @@ struct GemmShape {
   static constexpr int kRowsPerWave = NRT * 16;           // output rows (features) per wave
   static constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // output rows per workgroup
 };
+
+// Loads (vector-memory instructions) one wave issues per K tile, in order:
+// kActOps activation copies (kActGroups row groups + 1 scale copy), then
+// kWOps weight tiles, then for every fourth tile kWOps scale dwords (for the
+// next 4 tiles). The order is pinned (compiler barriers around each group).
+constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 terms, 4 waves)
+constexpr int kActOps = kActGroups + 1;
+constexpr int kWOps = 4;  // NM * NRT for both modes
+// Loads issued after the last activation copy of tile c, counted at the top
+// of the step that computes tile c (P = c % 4): tile c's weights, and the
+// scale dwords of c's group of 4 tiles when c starts one (they go out right
+// after). Copies complete in issue order with the other loads, so waiting
+// for the counter to drop to this value means the wave's copies of tile c
+// have landed in LDS.
+template <int P>
+constexpr int loads_after_act() {
+  return kWOps + (P == 0 ? kWOps : 0);  // tile c's weights (and scales when c starts a group)
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean "do not wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Keeps the machine scheduler from moving instructions across this point.
+__device__ __forceinline__ void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Returns its (wave-uniform) argument through a volatile asm statement. A
+// load whose address uses the result cannot be issued before the copies that
+// precede the call: the asm stays ordered after them, and the load depends on
+// it. (Loads may still be issued later than counted, which only makes the
+// counted waits stricter.)
+__device__ __forceinline__ int after_copies(int v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load); the caller has already waited for the
+// loads the other waves need.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct TileInfo {
   int e, row0, cnt, base;  // expert, first row within the expert, tokens, offsets[e]
@@ -188,8 +253,8 @@ __device__ __forceinline__ bool load_tile(int tile, const int32_t* tiles, const 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 struct ActLds {
-  uint8_t a[2][kTileM][kActRow];  // activation terms, swizzled
-  uint8_t s[2][kTileM][kScRow];   // activation scales (E8M0), per 32-column block
+  uint8_t a[2][kTileM][kActRow];  // activation terms of one K tile, swizzled
+  uint8_t s[2][kTileM][kScRow];   // their E8M0 scales, one per 32-column block
 };
 
 template <int MODE>
@@ -200,14 +265,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     const uint8_t* __restrict__ act_lo, const uint8_t* __restrict__ acts_hi,
     const uint8_t* __restrict__ acts_lo, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, int nrb, uint8_t* __restrict__ out_hi,
+    const int32_t* __restrict__ ntiles, int nrb, uint32_t act_bytes, uint8_t* __restrict__ out_hi,
     uint8_t* __restrict__ out_lo, uint8_t* __restrict__ outs_hi, uint8_t* __restrict__ outs_lo,
     float* __restrict__ slots) {
   using G = GemmShape<MODE>;
   constexpr int NM = G::NM, NRT = G::NRT;
-  constexpr int NCT = 4;  // 16-token MFMA column tiles per wave
-  // two separately named buffers (not an array indexed by a runtime number)
-  // so reads of one need not wait for the direct-to-LDS loads filling the other
+  constexpr int NCT = kTileM / 16;  // 16-token MFMA column tiles per wave
+  // separately named buffers (not an array indexed by a runtime number) so
+  // reads of one need not wait for the direct-to-LDS copies filling others
   __shared__ __attribute__((aligned(16))) ActLds lds0;
   __shared__ __attribute__((aligned(16))) ActLds lds1;
   __shared__ int tok_lds[kTileM];
@@ -217,25 +282,28 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   TileInfo ti;
   if (!load_tile(tile, tiles, ntiles, offsets, ti)) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int nw = wave;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int r = lane & 15, g = lane >> 4;
   const int nb = K >> 5, KT = K >> 7, KG = (KT + 3) >> 2, RT = nrows >> 4;
-  const int row_base = rb * G::kRowsPerBlock;          // first output row of the block
-  const int w0 = row_base + nw * G::kRowsPerWave;       // first output row of this wave
-  const int m0 = 0;                                     // first tile token of this wave
-  const int nct = max(0, min(NCT, (ti.cnt - m0 + 15) >> 4));  // token tiles of this wave
-  const bool wave_on = (w0 < nrows) && (nct > 0);
+  const int row_base = rb * G::kRowsPerBlock;        // first output row of the block
+  const int w0 = row_base + wave * G::kRowsPerWave;   // first output row of this wave
+  constexpr int m0 = 0;                               // first tile token of this wave
+  const int nct = min(NCT, (ti.cnt + 15) >> 4);       // token tiles holding tokens
+  const bool wave_on = w0 < nrows;
 
-  // activation row (token for gate/up, sorted pair position for down) per tile row
+  // activation row (token for gate/up, sorted pair position for down) per
+  // tile row; rows past the tile's tokens repeat row 0 (loaded, never stored)
   if (tid < kTileM) {
     const int i = (tid < ti.cnt) ? tid : 0;
     tok_lds[tid] = (MODE == kGateUp) ? perm[ti.base + ti.row0 + i] / k : ti.base + ti.row0 + i;
   }
   __syncthreads();
 
-  // ---- weights: tile (rt, kt) of matrix m at wq[m] + ((e RT + rt) KT + kt) 1024 + 16 lane
-  const int rt0 = (wave_on ? w0 : 0) >> 4;  // first row tile of this wave
+  // ---- weights: tile (rt, kt) of matrix m at wq[m] + ((e RT + rt) KT + kt) 1024 + 16 lane.
+  // A wave past the last row loads (and ignores) the first rows instead, so
+  // every wave issues the same loads.
+  const int rt0 = (wave_on ? w0 : 0) >> 4;
   const uint8_t* wq_t[NM];
   const uint32_t* ws_t[NM];
 #pragma unroll
@@ -246,61 +314,71 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     ws_t[m] = reinterpret_cast<const uint32_t*>(sc + (((size_t)ti.e * RT + rt0) * KG) * 256) + lane;
   }
   struct WStage {
-    uint4 q[NM][NRT][kChunkTiles];
+    uint4 q[NM][NRT];
   };
-  auto w_load = [&](int c, int S, WStage& ws) {
+  auto w_issue = [&](int kt, WStage& ws) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int s = 0; s < kChunkTiles; ++s)
-          if (s < S)
-            ws.q[m][rt][s] = *reinterpret_cast<const uint4*>(
-                wq_t[m] + ((size_t)rt * KT + kChunkTiles * c + s) * 1024);
+        ws.q[m][rt] =
+            *reinterpret_cast<const uint4*>(wq_t[m] + ((size_t)rt * KT + kt) * 1024);
   };
-  // scale dwords of the current group of 4 K tiles (sw) and of the next
-  // (swn), loaded one iteration ahead so the MFMAs never wait on a load that
-  // was issued behind direct-to-LDS copies
-  int sw[NM][NRT], swn[NM][NRT];
-  auto s_load = [&](int kg, int (&dst)[NM][NRT]) {
+  // scale dwords of groups of 4 K tiles: even groups in sa, odd groups in sb
+  // (two named sets, each live across the loop, so no copy is needed)
+  int sa[NM][NRT], sb[NM][NRT];
+  auto s_issue = [&](int kg, int (&dst)[NM][NRT]) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) dst[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
   };
 
-  // ---- activations: wave instruction j = 8 wave + i (32 per chunk): term
-  // j / 16, token rows 4 (j % 16) .. +3; lane -> row + lane / 16, slot lane % 16
-  // holding piece slot ^ (row % 16). Scales: one 4-byte copy per lane, wave w
-  // -> term w / 2, rows 32 (w % 2) + lane / 2, half lane % 2.
-  const uint8_t* act_t = (wave < 2) ? act_hi : act_lo;
-  uint32_t asrc[8];
+  // ---- activations: wave w copies term w / 2, token rows 64 (w % 2) .. +63
+  // as 8 row groups of 8 (lane -> row + lane / 8, slot lane % 8 holding piece
+  // slot ^ (row % 8)). A row group past the tile's tokens is given an offset
+  // beyond the buffer: the copy then reads nothing and writes zeros, so no
+  // copy sits behind a branch and none repeats another's bytes. Scales: wave
+  // w copies rows 64 (w / 2) .. +63 of term w % 2 (4 bytes per lane).
+  const int term = wave >> 1;
+  const int rbase = 64 * (wave & 1);
+  // buffer resources over the activation planes (MUBUF copies, bounds-checked
+  // against the plane size; word 3 = 32-bit data format, as untyped buffer
+  // loads on this family require)
+  const __amdgpu_buffer_rsrc_t act_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(term ? act_lo : act_hi), 0, (int)act_bytes, 0x00020000);
+  const int sterm = wave & 1;
+  const int srow0 = 64 * (wave >> 1);
+  const __amdgpu_buffer_rsrc_t sc_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(sterm ? acts_lo : acts_hi), 0, (int)(act_bytes >> 5), 0x00020000);
+  constexpr uint32_t kNoRead = 0x7fff0000u;  // beyond any plane (plane bytes < 2^31 - 2^16)
+  uint32_t asrc[kActGroups];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = 8 * wave + i;
-    const int row = 4 * (j & 15) + (lane >> 4);
-    asrc[i] = (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+  for (int i = 0; i < kActGroups; ++i) {
+    const int row = rbase + 8 * i + (lane >> 3);
+    asrc[i] = (rbase + 8 * i < ti.cnt)
+                  ? (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (row & 7))
+                  : kNoRead;
   }
-  const int sc_row = 32 * (wave & 1) + (lane >> 1);
-  const uint8_t* sc_src = ((wave < 2) ? acts_hi : acts_lo) + (size_t)tok_lds[sc_row] * nb;
-  auto act_issue = [&](ActLds& L, int c, int S) {
-    const uint32_t kb = (uint32_t)(kChunkTiles * c) * 128u;  // first column of the chunk
+  const uint32_t sc_off = (uint32_t)tok_lds[srow0 + lane] * (uint32_t)nb;
+  auto act_issue = [&](ActLds& L, int kt) {
+    const int kb = kt * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 8 * wave + i;
-      const int term = j >> 4, row0 = 4 * (j & 15);
-      if (row0 < ti.cnt) {
-        uint32_t off = asrc[i] + kb;
-        if (S < kChunkTiles) off -= 16u * (((lane & 15) ^ ((row0 + (lane >> 4)) & 15)) & 8u);
-        __builtin_amdgcn_global_load_lds(act_t + off, (lds_ptr)&L.a[term][row0][0], 16, 0, 0);
-      }
-    }
-    {
-      const int half = (S < kChunkTiles) ? 0 : (lane & 1);
-      __builtin_amdgcn_global_load_lds(sc_src + (kb >> 5) + 4 * half,
-                                       (lds_ptr)&L.s[wave >> 1][32 * (wave & 1)][0], 4, 0, 0);
-    }
+    for (int i = 0; i < kActGroups; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_ptr)&L.a[term][rbase + 8 * i][0], 16,
+                                               (int)asrc[i], kb, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_rs, (lds_ptr)&L.s[sterm][srow0][0], 4, (int)sc_off,
+                                             4 * kt, 0, 0);
+  };
+  // one ring stage: copy of tile kt, then its weights (clamped to the last
+  // tile so the tail issues the same loads; those stages are never read)
+  auto stage_issue = [&](ActLds& L, WStage& ws, int kt) {
+    kt = min(kt, KT - 1);
+    issue_fence();
+    act_issue(L, kt);
+    issue_fence();
+    w_issue(after_copies(kt), ws);
+    issue_fence();
   };
 
   v4f acc[NM][NRT][NCT];
@@ -311,91 +389,99 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // one chunk of MFMAs; SEL = byte of the scale dwords for step 0 (0 or 2)
-  auto compute = [&](const ActLds& L, int S, const WStage& ws, int sel) {
+  // B operands of one 16-token column tile: pieces g and 4 + g of the token
+  // row (K slots 16g.. and 64 + 16g.. of the MFMA), both terms, and the
+  // terms' scales of 32-column block g
+  struct BFrag {
+    v8i hi, lo;
+    int shi, slo;
+  };
+  auto b_load = [&](const ActLds& L, int ct, BFrag& b) {
+    const int tr = m0 + 16 * ct + r;
+    const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
+    b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
+                       *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
+    b.lo = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
+                       *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
+    b.shi = L.s[0][tr][g];
+    b.slo = L.s[1][tr][g];
+  };
+  // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
+  // next column tile's B operands are read while this one's MFMAs run.
+  auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc) {
+    constexpr int P = decltype(pc)::value;
+    BFrag b[2];
+    b_load(L, 0, b[0]);
 #pragma unroll
-    for (int s = 0; s < kChunkTiles; ++s) {
-      if (s >= S) break;
-      // pieces of slot-blocks g/2 and 2 + g/2 of tile s (token row % 16 == r)
-      const int c0 = 16 * ((8 * s + g) ^ r);
-      const int c1 = 16 * ((8 * s + 4 + g) ^ r);
-      const int sb = 4 * s + g;
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (ct < nct) {
+        if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
+        const BFrag& cb = b[ct & 1];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        if (ct < nct) {
-          const int tr = m0 + 16 * ct + r;
-          const v8i bh = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
-                                     *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
-          const v8i bl = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
-                                     *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
-          const int sh = L.s[0][tr][sb];
-          const int sl = L.s[1][tr][sb];
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int m = 0; m < NM; ++m)
+          for (int rt = 0; rt < NRT; ++rt)
+            acc[m][rt][ct] =
+                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.hi, cb.shi, acc[m][rt][ct]);
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-              const v8i a = fp4_operand(ws.q[m][rt][s]);
-              // scale byte (sel + s) of the A scale dword
-              if (sel + s == 0) {
-                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<0>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
-              } else if (sel + s == 1) {
-                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<1>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
-              } else if (sel + s == 2) {
-                acc[m][rt][ct] = mfma_fp4_fp8<2>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<2>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
-              } else {
-                acc[m][rt][ct] = mfma_fp4_fp8<3>(a, sw[m][rt], bh, sh, acc[m][rt][ct]);
-                acc[m][rt][ct] = mfma_fp4_fp8<3>(a, sw[m][rt], bl, sl, acc[m][rt][ct]);
-              }
-            }
-        }
-        // keep one column tile's B fragments live at a time
-        __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            acc[m][rt][ct] =
+                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.lo, cb.slo, acc[m][rt][ct]);
       }
     }
   };
 
-  // K loop, two chunks (= one scale group of 4 K tiles) per iteration so each
-  // LDS buffer and each scale byte is named statically.
-  const int nchunks = (KT + kChunkTiles - 1) / kChunkTiles;
-  auto tiles_of = [&](int c) { return min(kChunkTiles, KT - kChunkTiles * c); };
+  // ---- K loop, two stages: tile c in buffer c % 2 and weight set c % 2;
+  // scale dwords of even groups of 4 tiles in sa, odd groups in sb. Step P
+  // (= c % 8): wait for tile c's copies, barrier, issue tile c + 1 into the
+  // other stage (with its group's scale dwords when c + 1 starts a group),
+  // compute tile c.
+  auto step = [&](auto pc, const ActLds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
+                  ActLds& Ln, WStage& Wn, int kn) {
+    constexpr int P = decltype(pc)::value;
+    wait_vmcnt<loads_after_act<P & 3>()>();
+    stage_barrier();
+    stage_issue(Ln, Wn, kn);
+    if constexpr ((P & 3) == 3) {
+      s_issue(after_copies(min(kn >> 2, KG - 1)), P == 3 ? sb : sa);
+      issue_fence();
+    }
+    compute(Lc, Wc, sc, std::integral_constant<int, P & 3>());
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
   WStage wa, wb;
-  act_issue(lds0, 0, tiles_of(0));
-  if (wave_on) {
-    w_load(0, tiles_of(0), wa);
-    s_load(0, sw);
+  stage_issue(lds0, wa, 0);
+  s_issue(0, sa);
+  issue_fence();
+  for (int c = 0; c < KT; c += 8) {
+    step(I0(), lds0, wa, sa, lds1, wb, c + 1);
+    if (c + 1 >= KT) break;
+    step(I1(), lds1, wb, sa, lds0, wa, c + 2);
+    if (c + 2 >= KT) break;
+    step(I2(), lds0, wa, sa, lds1, wb, c + 3);
+    if (c + 3 >= KT) break;
+    step(I3(), lds1, wb, sa, lds0, wa, c + 4);
+    if (c + 4 >= KT) break;
+    step(I4(), lds0, wa, sb, lds1, wb, c + 5);
+    if (c + 5 >= KT) break;
+    step(I5(), lds1, wb, sb, lds0, wa, c + 6);
+    if (c + 6 >= KT) break;
+    step(I6(), lds0, wa, sb, lds1, wb, c + 7);
+    if (c + 7 >= KT) break;
+    step(I7(), lds1, wb, sb, lds0, wa, c + 8);
   }
-  __syncthreads();  // also waits for this thread's direct-to-LDS loads
-  for (int c = 0; c < nchunks; c += 2) {
-    {  // even chunk c: buffer 0, weights wa, scale bytes 0/1
-      const bool more = (c + 1) < nchunks;
-      if (more) {
-        act_issue(lds1, c + 1, tiles_of(c + 1));
-        if (wave_on) w_load(c + 1, tiles_of(c + 1), wb);
-      }
-      if (wave_on) compute(lds0, tiles_of(c), wa, 0);
-      __syncthreads();
-      if (!more) break;
-    }
-    {  // odd chunk c + 1: buffer 1, weights wb, scale bytes 2/3
-      const bool more = (c + 2) < nchunks;
-      if (more) {
-        act_issue(lds0, c + 2, tiles_of(c + 2));
-        if (wave_on) {
-          w_load(c + 2, tiles_of(c + 2), wa);
-          s_load((c + 2) >> 1, swn);
-        }
-      }
-      if (wave_on) compute(lds1, tiles_of(c + 1), wb, 2);
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) sw[m][rt] = swn[m][rt];
-    }
-  }
+  // no copy may still be writing this workgroup's LDS when it exits. (A
+  // wave past the last row computed on the first rows' weights: discarded.)
+  wait_vmcnt<0>();
   if (!wave_on) return;
 
   if (MODE == kGateUp) {
@@ -510,7 +596,7 @@ hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, con
   const int nrb = s.f / GemmShape<kGateUp>::kRowsPerBlock;
   hipLaunchKernelGGL(mx_gemm_kernel<kGateUp>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
                      st, s.d, s.f, s.f, s.k, w.gate_q, w.gate_s, w.up_q, w.up_s, xq, xq + xplane,
-                     xs, xs + xsplane, offsets, perm, tiles, ntiles, nrb, hq, hq + hplane, hs,
+                     xs, xs + xsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)xplane, hq, hq + hplane, hs,
                      hs + hsplane, nullptr);
   return hipGetLastError();
 }
@@ -526,7 +612,7 @@ hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const
   const int nrb = (s.d + rpb - 1) / rpb;
   hipLaunchKernelGGL(mx_gemm_kernel<kDown>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
                      st, s.f, s.d, s.f, s.k, w.down_q, w.down_s, nullptr, nullptr, hq, hq + hplane,
-                     hs, hs + hsplane, offsets, perm, tiles, ntiles, nrb, nullptr, nullptr, nullptr,
+                     hs, hs + hsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)hplane, nullptr, nullptr, nullptr,
                      nullptr, slots);
   return hipGetLastError();
 }
