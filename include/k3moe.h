@@ -188,7 +188,7 @@ int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K);
  * then releases the events. The stages: */
 #define K3MOE_STAGE_ROUTER_LOGITS 0  /* router logits (one kernel) */
 #define K3MOE_STAGE_TOPK          1  /* top-k + gates (one kernel) */
-#define K3MOE_STAGE_GROUP         2  /* histogram, scan, permute (three kernels) */
+#define K3MOE_STAGE_GROUP         2  /* histogram, block prefix, expert scan, permute (four kernels) */
 #define K3MOE_STAGE_QUANT_X       3  /* activation split for the MFMA path (one kernel) */
 #define K3MOE_STAGE_GATEUP        4  /* gate/up projection + SwiGLU (one kernel) */
 #define K3MOE_STAGE_COMBINE       5  /* gate-weighted sum of the k expert outputs (one kernel) */
