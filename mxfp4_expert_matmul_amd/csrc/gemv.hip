@@ -121,21 +121,22 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 }
 
 // down + combine: workgroup = one token x one 16-row tile of the output; its
-// 4 waves split the token's k slots (wave w: j = w, w + 4, ...). For each
+// 8 waves split the token's k slots (wave w: j = w, w + 8, ...). For each
 // slot a wave issues the loads of all its K tiles (the next slot's are issued
 // before the current one is computed), stages the pair's h (fp32) in its own
 // LDS region and reads each 32-value block of it as a broadcast. Lane (r, g)
 // keeps a gate-weighted partial of row 16 rt + r over K block g of every
 // tile; partials meet across lane groups, then across waves in fixed order.
 // Deterministic, no atomics.
-// grid: (T, d / 16), block 256, dynamic LDS 16 f bytes.
-constexpr int kDownTiles = 8;  // K tiles per step (a slot of f = 2048 takes 2 steps)
-__global__ __launch_bounds__(256) void gemv_down_kernel(
+// grid: (T, d / 16), block 512, dynamic LDS 32 f bytes.
+constexpr int kDownTiles = 4;  // K tiles per step (a slot of f = 2048 takes 4 steps)
+constexpr int kDownWaves = 8;
+__global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ h32, float* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) float hl[];  // [4][f]
-  __shared__ float red[4][16];
+  extern __shared__ __attribute__((aligned(16))) float hl[];  // [kDownWaves][f]
+  __shared__ float red[kDownWaves][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t = blockIdx.x, rt = blockIdx.y;
@@ -193,11 +194,11 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   // the wave's (slot, 16-tile chunk) steps; step s+1's weights are issued
   // after step s's h is loaded and before step s is computed
   const int nchunk = (KT + kDownTiles - 1) / kDownTiles;
-  const int nslot = (k - wave + 3) / 4;  // slots wave, wave + 4, ...
+  const int nslot = (k - wave + kDownWaves - 1) / kDownWaves;  // slots wave, wave + 8, ...
   const int nstep = nslot * nchunk;
   Slot sa, sb;
   auto step = [&](int s, Slot& cur, Slot& nxt) {
-    const int j = wave + 4 * (s / nchunk), kt0 = kDownTiles * (s % nchunk);
+    const int j = wave + kDownWaves * (s / nchunk), kt0 = kDownTiles * (s % nchunk);
     const bool on = valid(j);
     const bool stage = on && kt0 == 0;
     const float4* hsrc = reinterpret_cast<const float4*>(h32 + (size_t)(t * k + j) * f);
@@ -212,7 +213,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
       hr6 = hsrc[min(lane + 384, n4 - 1)];
       hr7 = hsrc[min(lane + 448, n4 - 1)];
     }
-    if (s + 1 < nstep) issue(wave + 4 * ((s + 1) / nchunk), kDownTiles * ((s + 1) % nchunk), nxt);
+    if (s + 1 < nstep)
+      issue(wave + kDownWaves * ((s + 1) / nchunk), kDownTiles * ((s + 1) % nchunk), nxt);
     if (!on) return;
     if (stage) {
       float4* hd = reinterpret_cast<float4*>(hw);
@@ -238,7 +240,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   if (g == 0) red[wave][r] = acc;
   __syncthreads();
   if (tid < 16) {
-    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    float s = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < kDownWaves; ++w) s += red[w][tid];
     y[(size_t)t * d + 16 * rt + tid] = s;
   }
 }
@@ -254,14 +258,15 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
 
 hipError_t prepare_gemv(const Shape& s) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 16 * s.f);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 4 * kDownWaves * s.f);
 }
 
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   dim3 g2(T, s.d / 16);
-  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(256), (size_t)16 * s.f, st, s.d, s.f, s.k, s.E,
+  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(64 * kDownWaves), (size_t)4 * kDownWaves * s.f, st,
+                     s.d, s.f, s.k, s.E,
                      w.down_q, w.down_s, idx, gate, h32, y);
   return hipGetLastError();
 }

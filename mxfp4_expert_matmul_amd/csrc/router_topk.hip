@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     if (t < T) {
-      float s = wave_sum(acc[t]);
+      const float s = wave_sum_dpp(acc[t]);
       if (lane == 0) part[wave][t] = s;
     }
   }
@@ -328,8 +328,13 @@ __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand,
   }
   if (c <= 64) {
     const uint64_t mine = lane < c ? cand[lane] : 0ull;
-    int rank = 0;
-    for (int i = 0; i < c; ++i) rank += cand[i] > mine ? 1 : 0;
+    int rank = 0;  // passing keys above mine, each broadcast from its lane
+    for (int i = 0; i < c; ++i) {
+      const uint64_t o =
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), i) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, i);
+      rank += o > mine ? 1 : 0;
+    }
     if (lane < c && rank < k) sel[rank] = mine;
     return lane < k ? sel[lane] : 0ull;
   }
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const float v = topk_key_value(mine);
   const float vmax = __shfl(v, 0, 64);
   const float w = (lane < k) ? expf(v - vmax) : 0.0f;
-  const float sum = wave_sum(w);
+  const float sum = wave_sum_dpp(w);
   if (lane < k) {
     idx[(size_t)t * k + lane] = topk_key_index(mine);
     gate[(size_t)t * k + lane] = w / sum;
