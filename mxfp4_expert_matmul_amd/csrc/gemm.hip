@@ -104,8 +104,8 @@ hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t*
 }
 
 // ------------------------------------------------------------- MFMA helpers
-__device__ __forceinline__ v8i fp4_operand(const uint4 q) {
-  v8i a = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+__device__ __forceinline__ v8i fp4_operand(const v4i q) {
+  v8i a = {q[0], q[1], q[2], q[3], 0, 0, 0, 0};
   return a;
 }
 
@@ -122,37 +122,40 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c)
 }
 
 // ------------------------------------------------------------- grouped GEMM
-// One workgroup = 4 waves = one (tile, row block): up to kTileM = 128 tokens
+// One workgroup = 4 waves = one (tile, row block): up to kTileM = 96 tokens
 // of one expert (a tile of the grouped pairs) times a block of weight rows.
-// At the long-prefill shapes an expert holds 50-130 tokens, so a tile is
-// nearly always a whole expert and its weights are read from HBM once.
+// At the long-prefill shapes an expert holds 50-100 tokens, so a tile is
+// nearly always a whole expert and its weights are read from HBM once
+// (96-token tiles leave room for a deeper weight ring than 128-token ones).
 //   gate/up (kGateUp): 128 features = 128 gate rows + the same 128 up rows;
 //   down    (kDown):   256 output rows.
 // Wave w owns 32 features (gate/up: two 16-row MFMA tiles of gate and the
 // same two of up, so SwiGLU pairs sit in one lane) or 64 rows (down: four
-// 16-row tiles), for all 128 tokens of the tile (eight 16-column MFMA
-// tiles). No two loads of a workgroup read the same bytes: a request for a
-// line that is still in flight stalls the CU's load path.
+// 16-row tiles), for all 96 tokens of the tile (six 16-column MFMA tiles).
+// No two loads of a workgroup read the same bytes: a request for a line
+// that is still in flight stalls the CU's load path.
 //
-// Two workgroups share a CU (66 KB of LDS and at most 256 registers per
+// Two workgroups share a CU (51 KB of LDS and at most 256 registers per
 // lane each), so one computes while the other waits for memory. K is walked
-// one 128-column tile at a time through two stages, the next tile's loads
-// issued before the current tile's MFMAs:
-//  - weights (tiled layout, layout.hip) go straight to registers: one MFMA A
-//    operand is one 1 KB tile, one coalesced 16-byte-per-lane load; a scale
-//    dword per lane covers 4 K tiles and is fetched with the group's first;
+// one 128-column tile at a time:
+//  - weights (tiled layout, layout.hip) go straight to registers through a
+//    ring of kWStages register sets, issued three tiles ahead: one MFMA A
+//    operand is one 1 KB tile, one coalesced 16-byte-per-lane buffer load; a
+//    scale dword per lane covers 4 K tiles and is fetched with the group's
+//    first;
 //  - activations (two E4M3 terms + scales) of the tile's tokens are copied
-//    once per workgroup straight into LDS (global_load_lds; 16-byte piece p
-//    of token row t at slot p ^ (t % 8), so the 16 lanes of an MFMA column
-//    group read distinct bank groups).
-// Every wave issues the same number of loads per stage, so a stage is known
+//    once per workgroup straight into LDS (buffer loads to LDS, two stages,
+//    one tile ahead; 16-byte piece p of token row t at slot p ^ (t % 8), so
+//    the 16 lanes of an MFMA column group read distinct bank groups).
+// Every wave issues the same number of loads per step, so a stage is known
 // complete by waiting on the wave's load counter down to the count issued
 // after it (s_waitcnt vmcnt(N)), followed by a plain workgroup barrier; the
 // loads of the next stages stay in flight across it (a __syncthreads would
 // wait for all of them).
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
-constexpr int kStages = 2;                 // ring depth (LDS buffers, weight register sets)
+constexpr int kStages = 2;                 // activation ring depth (LDS buffers)
+constexpr int kWStages = 4;                // weight ring depth (register sets)
 constexpr int kActRow = 128;               // LDS bytes per token row and term (one K tile)
 constexpr int kScRow = 4;                  // scale bytes per token row and term (4 blocks)
 constexpr int kThreads = 256;
@@ -170,6 +173,8 @@ struct GemmShape {
 // kWOps weight tiles, then for every fourth tile kWOps scale dwords (for the
 // next 4 tiles). The order is pinned (compiler barriers around each group).
 constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 terms, 4 waves)
+constexpr int kScRows = 128;  // scale rows per term in LDS: two waves copy 64 each (rows past
+                              // the tile's tokens read nothing)
 constexpr int kActOps = kActGroups + 1;
 constexpr int kWOps = 4;  // NM * NRT for both modes
 // Loads issued after the last activation copy of tile c, counted at the top
@@ -178,9 +183,12 @@ constexpr int kWOps = 4;  // NM * NRT for both modes
 // after). Copies complete in issue order with the other loads, so waiting
 // for the counter to drop to this value means the wave's copies of tile c
 // have landed in LDS.
+// Tile c's copies go out one step before the step that computes it,
+// followed by the weights of tile c + kWStages - 1 (and their group's scale
+// dwords when that tile starts a group of 4).
 template <int P>
 constexpr int loads_after_act() {
-  return kWOps + (P == 0 ? kWOps : 0);  // tile c's weights (and scales when c starts a group)
+  return kWOps + (((P + kWStages - 2) & 3) == 0 ? kWOps : 0);
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
@@ -254,7 +262,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 struct ActLds {
   uint8_t a[2][kTileM][kActRow];  // activation terms of one K tile, swizzled
-  uint8_t s[2][kTileM][kScRow];   // their E8M0 scales, one per 32-column block
+  uint8_t s[2][kScRows][kScRow];  // their E8M0 scales, one per 32-column block
 };
 
 template <int MODE>
@@ -303,26 +311,33 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // ---- weights: tile (rt, kt) of matrix m at wq[m] + ((e RT + rt) KT + kt) 1024 + 16 lane.
   // A wave past the last row loads (and ignores) the first rows instead, so
   // every wave issues the same loads.
+  // Weight loads go through a buffer over the wave's NRT row tiles, so the
+  // ring's look-ahead past the last K tile reads nothing (an offset past the
+  // buffer returns zeros without a memory access).
   const int rt0 = (wave_on ? w0 : 0) >> 4;
-  const uint8_t* wq_t[NM];
+  constexpr uint32_t kNoRead = 0x7fff0000u;  // beyond any buffer here (all < 2^31 - 2^16)
+  __amdgpu_buffer_rsrc_t wq_rs[NM];
   const uint32_t* ws_t[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const uint8_t* q = (m == 0) ? wq0 : wq1;
     const uint8_t* sc = (m == 0) ? ws0 : ws1;
-    wq_t[m] = q + (((size_t)ti.e * RT + rt0) * KT) * 1024 + 16 * lane;
+    wq_rs[m] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(q + (((size_t)ti.e * RT + rt0) * KT) * 1024), 0, NRT * KT * 1024,
+        0x00020000);
     ws_t[m] = reinterpret_cast<const uint32_t*>(sc + (((size_t)ti.e * RT + rt0) * KG) * 256) + lane;
   }
   struct WStage {
-    uint4 q[NM][NRT];
+    v4i q[NM][NRT];
   };
   auto w_issue = [&](int kt, WStage& ws) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        ws.q[m][rt] =
-            *reinterpret_cast<const uint4*>(wq_t[m] + ((size_t)rt * KT + kt) * 1024);
+        ws.q[m][rt] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                     wq_rs[m], kt < KT ? 16 * lane + (rt * KT + kt) * 1024 : (int)kNoRead, 0, 0));
   };
   // scale dwords of groups of 4 K tiles: even groups in sa, odd groups in sb
   // (two named sets, each live across the loop, so no copy is needed)
@@ -341,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // copy sits behind a branch and none repeats another's bytes. Scales: wave
   // w copies rows 64 (w / 2) .. +63 of term w % 2 (4 bytes per lane).
   const int term = wave >> 1;
-  const int rbase = 64 * (wave & 1);
+  const int rbase = (kTileM / 2) * (wave & 1);
   // buffer resources over the activation planes (MUBUF copies, bounds-checked
   // against the plane size; word 3 = 32-bit data format, as untyped buffer
   // loads on this family require)
@@ -351,7 +366,6 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   const int srow0 = 64 * (wave >> 1);
   const __amdgpu_buffer_rsrc_t sc_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(sterm ? acts_lo : acts_hi), 0, (int)(act_bytes >> 5), 0x00020000);
-  constexpr uint32_t kNoRead = 0x7fff0000u;  // beyond any plane (plane bytes < 2^31 - 2^16)
   uint32_t asrc[kActGroups];
 #pragma unroll
   for (int i = 0; i < kActGroups; ++i) {
@@ -360,7 +374,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
                   ? (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (row & 7))
                   : kNoRead;
   }
-  const uint32_t sc_off = (uint32_t)tok_lds[srow0 + lane] * (uint32_t)nb;
+  const int srow = srow0 + lane;
+  const uint32_t sc_off = srow < ti.cnt ? (uint32_t)tok_lds[srow] * (uint32_t)nb : kNoRead;
   auto act_issue = [&](ActLds& L, int kt) {
     const int kb = kt * 128;
 #pragma unroll
@@ -370,14 +385,15 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_rs, (lds_ptr)&L.s[sterm][srow0][0], 4, (int)sc_off,
                                              4 * kt, 0, 0);
   };
-  // one ring stage: copy of tile kt, then its weights (clamped to the last
-  // tile so the tail issues the same loads; those stages are never read)
-  auto stage_issue = [&](ActLds& L, WStage& ws, int kt) {
-    kt = min(kt, KT - 1);
+  // one step's loads: the copy of tile ka (clamped to the last tile so the
+  // tail issues the same loads; that stage is never read), then the weights
+  // of tile kw (nothing past the last tile)
+  auto stage_issue = [&](ActLds& L, int ka, WStage& ws, int kw) {
+    ka = min(ka, KT - 1);
     issue_fence();
-    act_issue(L, kt);
+    act_issue(L, ka);
     issue_fence();
-    w_issue(after_copies(kt), ws);
+    w_issue(after_copies(kw), ws);
     issue_fence();
   };
 
@@ -433,19 +449,21 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     }
   };
 
-  // ---- K loop, two stages: tile c in buffer c % 2 and weight set c % 2;
-  // scale dwords of even groups of 4 tiles in sa, odd groups in sb. Step P
-  // (= c % 8): wait for tile c's copies, barrier, issue tile c + 1 into the
-  // other stage (with its group's scale dwords when c + 1 starts a group),
-  // compute tile c.
+  // ---- K loop: tile c's activations in LDS buffer c % 2, its weights in
+  // register set c % 4 (issued three steps ahead); scale dwords of even
+  // groups of 4 tiles in sa, odd groups in sb. Step P (= c % 8): wait for
+  // tile c's copies (its weights, issued earlier, have landed too), barrier,
+  // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
+  // group's scale dwords when c + 3 starts one), compute tile c.
   auto step = [&](auto pc, const ActLds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
-                  ActLds& Ln, WStage& Wn, int kn) {
+                  ActLds& Ln, WStage& Wn, int c) {
     constexpr int P = decltype(pc)::value;
-    wait_vmcnt<loads_after_act<P & 3>()>();
+    wait_vmcnt<loads_after_act<P>()>();
     stage_barrier();
-    stage_issue(Ln, Wn, kn);
-    if constexpr ((P & 3) == 3) {
-      s_issue(after_copies(min(kn >> 2, KG - 1)), P == 3 ? sb : sa);
+    stage_issue(Ln, c + 1, Wn, c + kWStages - 1);
+    if constexpr (((P + kWStages - 1) & 3) == 0) {
+      s_issue(after_copies(min((c + kWStages - 1) >> 2, KG - 1)),
+              (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
       issue_fence();
     }
     compute(Lc, Wc, sc, std::integral_constant<int, P & 3>());
@@ -458,26 +476,31 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   using I5 = std::integral_constant<int, 5>;
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
-  WStage wa, wb;
-  stage_issue(lds0, wa, 0);
+  static_assert(kWStages == 4 && kStages == 2, "the unrolled ring below assumes these depths");
+  WStage wa, wb, wc, wd;
+  stage_issue(lds0, 0, wa, 0);
   s_issue(0, sa);
   issue_fence();
+  w_issue(1, wb);
+  issue_fence();
+  w_issue(2, wc);
+  issue_fence();
   for (int c = 0; c < KT; c += 8) {
-    step(I0(), lds0, wa, sa, lds1, wb, c + 1);
+    step(I0(), lds0, wa, sa, lds1, wd, c);
     if (c + 1 >= KT) break;
-    step(I1(), lds1, wb, sa, lds0, wa, c + 2);
+    step(I1(), lds1, wb, sa, lds0, wa, c + 1);
     if (c + 2 >= KT) break;
-    step(I2(), lds0, wa, sa, lds1, wb, c + 3);
+    step(I2(), lds0, wc, sa, lds1, wb, c + 2);
     if (c + 3 >= KT) break;
-    step(I3(), lds1, wb, sa, lds0, wa, c + 4);
+    step(I3(), lds1, wd, sa, lds0, wc, c + 3);
     if (c + 4 >= KT) break;
-    step(I4(), lds0, wa, sb, lds1, wb, c + 5);
+    step(I4(), lds0, wa, sb, lds1, wd, c + 4);
     if (c + 5 >= KT) break;
-    step(I5(), lds1, wb, sb, lds0, wa, c + 6);
+    step(I5(), lds1, wb, sb, lds0, wa, c + 5);
     if (c + 6 >= KT) break;
-    step(I6(), lds0, wa, sb, lds1, wb, c + 7);
+    step(I6(), lds0, wc, sb, lds1, wb, c + 6);
     if (c + 7 >= KT) break;
-    step(I7(), lds1, wb, sb, lds0, wa, c + 8);
+    step(I7(), lds1, wd, sb, lds0, wc, c + 7);
   }
   // no copy may still be writing this workgroup's LDS when it exits. (A
   // wave past the last row computed on the first rows' weights: discarded.)

@@ -13,6 +13,9 @@
 //   gemv_down:   per token and output row m:
 //       y[m] = sum_j gate_j * (Wd[e_j][m,:] . h_j)                        (fp32)
 // Both are deterministic (fixed summation order, no atomics).
+#include <type_traits>
+#include <utility>
+
 #include "k3_device.h"
 #include "k3_kernels.h"
 
@@ -121,120 +124,166 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 }
 
 // down + combine: workgroup = one token x one 16-row tile of the output; its
-// 8 waves split the token's k slots (wave w: j = w, w + 8, ...). For each
-// slot a wave issues the loads of all its K tiles (the next slot's are issued
-// before the current one is computed), stages the pair's h (fp32) in its own
-// LDS region and reads each 32-value block of it as a broadcast. Lane (r, g)
-// keeps a gate-weighted partial of row 16 rt + r over K block g of every
-// tile; partials meet across lane groups, then across waves in fixed order.
+// 8 waves split the token's k slots (wave w: j = w, w + 8, ...). A wave walks
+// its (slot, 4-tile chunk) steps with the weights of the next kDownDepth - 1
+// steps in flight while it computes the current one (a ring of register
+// sets). Every step issues the same five buffer loads (four 1 KB tiles and
+// one scale dword per lane); a load past the row tile's K extent, of a
+// dropped slot or past the wave's last slot is given an empty buffer and
+// reads zeros without touching memory (the whole offset is in the per-lane
+// part, which the buffer's size check covers), so every step issues the same
+// loads and the counted waits below are exact. At a slot's first step the pair's h
+// (fp32) goes through registers into the wave's own LDS region, and each
+// 32-value block of it is read back as a broadcast. Lane (r, g) keeps a
+// gate-weighted partial of row 16 rt + r over K block g of every tile;
+// partials meet across lane groups, then across waves in fixed order.
 // Deterministic, no atomics.
-// grid: (T, d / 16), block 512, dynamic LDS 32 f bytes.
+// grid: (T, d / 16), block 512, dynamic LDS 8 * 1 KB * HOPS.
 constexpr int kDownTiles = 4;  // K tiles per step (a slot of f = 2048 takes 4 steps)
 constexpr int kDownWaves = 8;
+constexpr int kDownDepth = 4;  // ring of weight register sets
+constexpr int kDownLoads = kDownTiles + 1;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 1 KB h pieces per slot (f <= 256 HOPS): the size of a wave's LDS region
+__host__ __device__ constexpr int down_h_ops(int f) {
+  return f <= 512 ? 2 : f <= 1024 ? 4 : f <= 2048 ? 8 : 16;
+}
+
+template <int N>
+__device__ __forceinline__ void down_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void down_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int V>
+using ic = std::integral_constant<int, V>;
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N - 1>{}): compile-time indices
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int HOPS>
 __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ h32, float* __restrict__ y) {
-  extern __shared__ __attribute__((aligned(16))) float hl[];  // [kDownWaves][f]
+  constexpr int NC = HOPS / 2;                                // steps per slot
+  constexpr int SPI = NC >= kDownDepth ? 1 : kDownDepth / NC;  // slots per loop iteration
+  constexpr int STEPS = SPI * NC;
+  static_assert(STEPS % kDownDepth == 0, "ring phase must repeat every iteration");
+  constexpr int HREGS = HOPS < 8 ? HOPS : 8;  // 1 KB h pieces held in registers at once
+  extern __shared__ __attribute__((aligned(16))) float hl[];  // [kDownWaves][256 * HOPS]
   __shared__ float red[kDownWaves][16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int t = blockIdx.x, rt = blockIdx.y;
   const int RT = d >> 4, KT = f >> 7, KG = (KT + 3) >> 2;
-  float* hw = hl + (size_t)wave * f;
-  struct Slot {
-    uint4 q[kDownTiles];
-    uint32_t sw[kDownTiles / 4];
+  float* hw = hl + (size_t)wave * 256 * HOPS;
+  struct Ring {
+    v4u q[kDownTiles];
+    uint32_t sw;
   };
-  // loads of K tiles kt0 .. kt0 + 15 of slot j's expert (nothing for a
-  // dropped slot)
-  auto issue = [&](int j, int kt0, Slot& sl) {
-    const int e = idx[(size_t)t * k + j];
-    if (e < 0 || e >= E) return;
-    const size_t tile0 = ((size_t)e * RT + rt) * KT;
-    const uint8_t* qt = dq + tile0 * 1024 + 16 * lane;
-    const uint32_t* st = reinterpret_cast<const uint32_t*>(ds + ((size_t)e * RT + rt) * KG * 256) + lane;
-    const int n = min(kDownTiles, KT - kt0);
+  const int nslot = (k - wave + kDownWaves - 1) / kDownWaves;  // slots wave, wave + 8, ...
+  const int niter = (nslot + SPI - 1) / SPI;
+  // expert of the wave's i-th slot, -1 past the last slot or for a dropped pair
+  auto expert_of = [&](int i) {
+    if (i >= nslot) return -1;
+    const int e = idx[(size_t)t * k + wave + kDownWaves * i];
+    return (e >= 0 && e < E) ? e : -1;
+  };
+  // the five loads of step s (slot s / NC, K tiles from 4 (s % NC))
+  auto issue = [&](int s, Ring& b) {
+    const int e = expert_of(s / NC), kt0 = kDownTiles * (s % NC);
+    const bool on = e >= 0;
+    const size_t row = on ? (size_t)e * RT + rt : 0;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(dq + row * KT * 1024), 0, on ? KT * 1024 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(ds + row * KG * 256), 0, on ? KG * 256 : 0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kDownTiles; ++i)
-      if (i < n) sl.q[i] = *reinterpret_cast<const uint4*>(qt + (size_t)(kt0 + i) * 1024);
+      b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane + 1024 * (kt0 + i), 0, 0);
+    b.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane + 256 * (kt0 >> 2), 0, 0);
+  };
+  // h of the wave's i-th slot, piece part: loads into registers (lanes past
+  // f, and slots with nothing to compute, read zeros), then LDS stores
+  auto h_load = [&](int i, int part, v4u (&hr)[HREGS]) {
+    const bool on = expert_of(i) >= 0;
+    const size_t pair = on ? (size_t)t * k + wave + kDownWaves * i : 0;
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(h32 + pair * f), 0, on ? 4 * f : 0, 0x00020000);
 #pragma unroll
-    for (int s2 = 0; s2 < kDownTiles / 4; ++s2)
-      if (4 * s2 < n) sl.sw[s2] = st[64 * ((kt0 >> 2) + s2)];
+    for (int v = 0; v < HREGS; ++v)
+      hr[v] = __builtin_amdgcn_raw_buffer_load_b128(rh, 16 * lane + 1024 * (HREGS * part + v), 0, 0);
+  };
+  auto h_store = [&](int part, const v4u (&hr)[HREGS]) {
+    v4u* hd = reinterpret_cast<v4u*>(hw + 256 * HREGS * part) + lane;
+#pragma unroll
+    for (int v = 0; v < HREGS; ++v) hd[64 * v] = hr[v];
   };
   float acc = 0.0f;
-  // h of slot j: its first 2048 values go through registers (loaded before
-  // the next step's weights, so waiting for them does not wait for those),
-  // the rest (f > 2048) straight into LDS
-  constexpr int kStageF4 = 8;  // float4 per lane held in registers
-  const int n4 = f >> 2;
-  auto compute = [&](int j, int kt0, const Slot& sl) {
-    const int pair = t * k + j;
-    const int n = min(kDownTiles, KT - kt0);
+  auto compute = [&](int i, int kt0, const Ring& b) {
     float pe = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kDownTiles; ++i)
-      if (i < n) {
-        const float4* hs = reinterpret_cast<const float4*>(hw + 128 * (kt0 + i) + 32 * g);
+    for (int u = 0; u < kDownTiles; ++u)
+      if (kt0 + u < KT) {
+        const float4* hs = reinterpret_cast<const float4*>(hw + 128 * (kt0 + u) + 32 * g);
         float hv[32];
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const float4 h4 = hs[v];
           hv[4 * v] = h4.x; hv[4 * v + 1] = h4.y; hv[4 * v + 2] = h4.z; hv[4 * v + 3] = h4.w;
         }
-        pe = fmaf(block_dot_f32(sl.q[i], hv),
-                  e8m0_to_f32((sl.sw[i >> 2] >> (8 * (i & 3))) & 0xffu), pe);
+        const uint4 q = {b.q[u].x, b.q[u].y, b.q[u].z, b.q[u].w};
+        pe = fmaf(block_dot_f32(q, hv), e8m0_to_f32((b.sw >> (8 * u)) & 0xffu), pe);
       }
-    acc = fmaf(gate[pair], pe, acc);
+    acc = fmaf(gate[(size_t)t * k + wave + kDownWaves * i], pe, acc);
   };
-  auto valid = [&](int j) {
-    const int e = idx[(size_t)t * k + j];
-    return e >= 0 && e < E;  // a dropped pair contributes zero
-  };
-  // the wave's (slot, 16-tile chunk) steps; step s+1's weights are issued
-  // after step s's h is loaded and before step s is computed
-  const int nchunk = (KT + kDownTiles - 1) / kDownTiles;
-  const int nslot = (k - wave + kDownWaves - 1) / kDownWaves;  // slots wave, wave + 8, ...
-  const int nstep = nslot * nchunk;
-  Slot sa, sb;
-  auto step = [&](int s, Slot& cur, Slot& nxt) {
-    const int j = wave + kDownWaves * (s / nchunk), kt0 = kDownTiles * (s % nchunk);
-    const bool on = valid(j);
-    const bool stage = on && kt0 == 0;
-    const float4* hsrc = reinterpret_cast<const float4*>(h32 + (size_t)(t * k + j) * f);
-    float4 hr0, hr1, hr2, hr3, hr4, hr5, hr6, hr7;  // lane + 64 v, v = 0..7 (clamped)
-    if (stage) {
-      hr0 = hsrc[min(lane, n4 - 1)];
-      hr1 = hsrc[min(lane + 64, n4 - 1)];
-      hr2 = hsrc[min(lane + 128, n4 - 1)];
-      hr3 = hsrc[min(lane + 192, n4 - 1)];
-      hr4 = hsrc[min(lane + 256, n4 - 1)];
-      hr5 = hsrc[min(lane + 320, n4 - 1)];
-      hr6 = hsrc[min(lane + 384, n4 - 1)];
-      hr7 = hsrc[min(lane + 448, n4 - 1)];
-    }
-    if (s + 1 < nstep)
-      issue(wave + kDownWaves * ((s + 1) / nchunk), kDownTiles * ((s + 1) % nchunk), nxt);
-    if (!on) return;
-    if (stage) {
-      float4* hd = reinterpret_cast<float4*>(hw);
-      if (lane < n4) hd[lane] = hr0;
-      if (lane + 64 < n4) hd[lane + 64] = hr1;
-      if (lane + 128 < n4) hd[lane + 128] = hr2;
-      if (lane + 192 < n4) hd[lane + 192] = hr3;
-      if (lane + 256 < n4) hd[lane + 256] = hr4;
-      if (lane + 320 < n4) hd[lane + 320] = hr5;
-      if (lane + 384 < n4) hd[lane + 384] = hr6;
-      if (lane + 448 < n4) hd[lane + 448] = hr7;
-      for (int i = lane + 64 * kStageF4; i < n4; i += 64) hd[i] = hsrc[i];
-    }
-    compute(j, kt0, cur);
-  };
-  if (nstep > 0) issue(wave, 0, sa);
-  for (int s = 0; s < nstep; s += 2) {
-    step(s, sa, sb);
-    if (s + 1 < nstep) step(s + 1, sb, sa);
+  Ring ring[kDownDepth];
+  static_for<kDownDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
+  for (int it = 0; it < niter; ++it) {
+    static_for<STEPS>([&](auto U) {
+      constexpr int u = U(), c = u % NC;
+      const int s = it * STEPS + u, i = it * SPI + u / NC;
+      Ring& cur = ring[u % kDownDepth];
+      Ring& fut = ring[(u + kDownDepth - 1) % kDownDepth];
+      down_fence();
+      if constexpr (c == 0) {  // the slot's h: registers, then the wave's LDS region
+        v4u hr[HREGS];
+        h_load(i, 0, hr);
+        down_fence();
+        issue(s + kDownDepth - 1, fut);
+        down_fence();
+        down_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
+        down_fence();
+        h_store(0, hr);
+        static_for<HOPS / HREGS - 1>([&](auto Q) {  // f > 2048: the rest of h
+          h_load(i, Q() + 1, hr);
+          down_fence();
+          down_wait_vmcnt<0>();
+          down_fence();
+          h_store(Q() + 1, hr);
+        });
+      } else {
+        issue(s + kDownDepth - 1, fut);
+        down_fence();
+        down_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads have landed
+        down_fence();
+      }
+      if (expert_of(i) >= 0) compute(i, kDownTiles * c, cur);
+    });
   }
+  down_wait_vmcnt<0>();
   acc += __shfl_xor(acc, 16, 64);
   acc += __shfl_xor(acc, 32, 64);
   if (g == 0) red[wave][r] = acc;
@@ -256,18 +305,38 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
   return hipGetLastError();
 }
 
+template <int HOPS>
+static hipError_t set_down_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel<HOPS>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kDownWaves * 1024 * HOPS);
+}
+
 hipError_t prepare_gemv(const Shape& s) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 4 * kDownWaves * s.f);
+  switch (down_h_ops(s.f)) {
+    case 2: return set_down_lds<2>();
+    case 4: return set_down_lds<4>();
+    case 8: return set_down_lds<8>();
+    default: return set_down_lds<16>();
+  }
 }
 
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  dim3 g2(T, s.d / 16);
-  hipLaunchKernelGGL(gemv_down_kernel, g2, dim3(64 * kDownWaves), (size_t)4 * kDownWaves * s.f, st,
-                     s.d, s.f, s.k, s.E,
-                     w.down_q, w.down_s, idx, gate, h32, y);
+  const dim3 grid(T, s.d / 16), block(64 * kDownWaves);
+  const int hops = down_h_ops(s.f);
+  const size_t lds = (size_t)kDownWaves * 1024 * hops;
+#define K3_DOWN(H)                                                                             \
+  hipLaunchKernelGGL(gemv_down_kernel<H>, grid, block, lds, st, s.d, s.f, s.k, s.E, w.down_q, \
+                     w.down_s, idx, gate, h32, y)
+  switch (hops) {
+    case 2: K3_DOWN(2); break;
+    case 4: K3_DOWN(4); break;
+    case 8: K3_DOWN(8); break;
+    default: K3_DOWN(16); break;
+  }
+#undef K3_DOWN
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 namespace k3 {
 
 // Prefill grouped GEMM tile: tokens (sorted pairs) per tile.
-constexpr int kTileM = 128;
+constexpr int kTileM = 96;
 // Pairs per block of the grouping step.
 constexpr int kGroupChunk = 256;
 // Largest T served by the GEMV (decode) expert path.
