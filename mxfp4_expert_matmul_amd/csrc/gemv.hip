@@ -9,7 +9,8 @@
 // each row over its four lane groups.
 //
 //   gemv_gateup: per (token, slot) pair and feature n:
-//       g = Wg[e][n,:] . x,  u = Wu[e][n,:] . x,  h[n] = SiLU(g) * u   (fp32)
+//       g = Wg[e][n,:] . x,  u = Wu[e][n,:] . x,  h[n] = SiLU(g) * u
+//       (fp32, stored rounded to bf16: relative error <= 2^-9)
 //   gemv_down:   per token and output row m:
 //       y[m] = sum_j gate_j * (Wd[e_j][m,:] . h_j)                        (fp32)
 // Both are deterministic (fixed summation order, no atomics).
@@ -71,7 +72,7 @@ __device__ __forceinline__ float block_dot_f32(const uint4 q, const float* hv) {
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
-    const int32_t* __restrict__ idx, float* __restrict__ h32) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ hb) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int pair = blockIdx.x;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   ga += __shfl_xor(ga, 32, 64);
   ua += __shfl_xor(ua, 16, 64);
   ua += __shfl_xor(ua, 32, 64);
-  if (g == 0) h32[(size_t)pair * f + 16 * rt + r] = silu_f32(ga) * ua;
+  if (g == 0) hb[(size_t)pair * f + 16 * rt + r] = f32_to_bf16_rne(silu_f32(ga) * ua);
 }
 
 // down + combine: workgroup = one token x one 16-row tile of the output; its
@@ -132,22 +133,24 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
 // dropped slot or past the wave's last slot is given an empty buffer and
 // reads zeros without touching memory (the whole offset is in the per-lane
 // part, which the buffer's size check covers), so every step issues the same
-// loads and the counted waits below are exact. At a slot's first step the pair's h
-// (fp32) goes through registers into the wave's own LDS region, and each
-// 32-value block of it is read back as a broadcast. Lane (r, g) keeps a
-// gate-weighted partial of row 16 rt + r over K block g of every tile;
-// partials meet across lane groups, then across waves in fixed order.
-// Deterministic, no atomics.
-// grid: (T, d / 16), block 512, dynamic LDS 8 * 1 KB * HOPS.
+// loads and the counted waits below are exact. The h (bf16) of two slots at
+// a time is copied straight into the wave's own LDS region (buffer loads to
+// LDS); with k <= 16 that happens once, before the first weights, so no step
+// waits for h. Each 32-value block of h is read back as a broadcast. Lane
+// (r, g) keeps a gate-weighted partial of row 16 rt + r over K block g of
+// every tile; partials meet across lane groups, then across waves in fixed
+// order. Deterministic, no atomics.
+// grid: (T, d / 16), block 512, dynamic LDS 8 waves x 2 slots x NC KB.
 constexpr int kDownTiles = 4;  // K tiles per step (a slot of f = 2048 takes 4 steps)
 constexpr int kDownWaves = 8;
 constexpr int kDownDepth = 4;  // ring of weight register sets
 constexpr int kDownLoads = kDownTiles + 1;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// 1 KB h pieces per slot (f <= 256 HOPS): the size of a wave's LDS region
-__host__ __device__ constexpr int down_h_ops(int f) {
-  return f <= 512 ? 2 : f <= 1024 ? 4 : f <= 2048 ? 8 : 16;
+// 4-tile chunks per slot (f <= 512 NC); a slot's bf16 h is NC KB
+__host__ __device__ constexpr int down_chunks(int f) {
+  return f <= 512 ? 1 : f <= 1024 ? 2 : f <= 2048 ? 4 : 8;
 }
 
 template <int N>
@@ -171,24 +174,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int HOPS>
+// MULTI: a wave has more than two slots (k > 16), so h is copied again
+// every second slot
+template <int NC, bool MULTI>
 __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
-    const float* __restrict__ h32, float* __restrict__ y) {
-  constexpr int NC = HOPS / 2;                                // steps per slot
+    const uint16_t* __restrict__ hb, float* __restrict__ y) {
   constexpr int SPI = NC >= kDownDepth ? 1 : kDownDepth / NC;  // slots per loop iteration
   constexpr int STEPS = SPI * NC;
   static_assert(STEPS % kDownDepth == 0, "ring phase must repeat every iteration");
-  constexpr int HREGS = HOPS < 8 ? HOPS : 8;  // 1 KB h pieces held in registers at once
-  extern __shared__ __attribute__((aligned(16))) float hl[];  // [kDownWaves][256 * HOPS]
+  constexpr int HSLOT = 512 * NC;  // bf16 values of one slot's LDS region
+  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];  // [kDownWaves][2][HSLOT]
   __shared__ float red[kDownWaves][16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int t = blockIdx.x, rt = blockIdx.y;
   const int RT = d >> 4, KT = f >> 7, KG = (KT + 3) >> 2;
-  float* hw = hl + (size_t)wave * 256 * HOPS;
+  uint16_t* hw = hl + (size_t)wave * 2 * HSLOT;
   struct Ring {
     v4u q[kDownTiles];
     uint32_t sw;
@@ -215,21 +219,17 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
       b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane + 1024 * (kt0 + i), 0, 0);
     b.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane + 256 * (kt0 >> 2), 0, 0);
   };
-  // h of the wave's i-th slot, piece part: loads into registers (lanes past
-  // f, and slots with nothing to compute, read zeros), then LDS stores
-  auto h_load = [&](int i, int part, v4u (&hr)[HREGS]) {
+  // h of the wave's i-th slot -> its LDS region (NC copies of 1 KB; values
+  // past f, and slots with nothing to compute, read as zeros)
+  auto h_copy = [&](int i) {
     const bool on = expert_of(i) >= 0;
     const size_t pair = on ? (size_t)t * k + wave + kDownWaves * i : 0;
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(h32 + pair * f), 0, on ? 4 * f : 0, 0x00020000);
+        const_cast<uint16_t*>(hb + pair * f), 0, on ? 2 * f : 0, 0x00020000);
 #pragma unroll
-    for (int v = 0; v < HREGS; ++v)
-      hr[v] = __builtin_amdgcn_raw_buffer_load_b128(rh, 16 * lane + 1024 * (HREGS * part + v), 0, 0);
-  };
-  auto h_store = [&](int part, const v4u (&hr)[HREGS]) {
-    v4u* hd = reinterpret_cast<v4u*>(hw + 256 * HREGS * part) + lane;
-#pragma unroll
-    for (int v = 0; v < HREGS; ++v) hd[64 * v] = hr[v];
+    for (int v = 0; v < NC; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_ptr)(hw + (i & 1) * HSLOT + 512 * v),
+                                               16, 16 * lane + 1024 * v, 0, 0, 0);
   };
   float acc = 0.0f;
   auto compute = [&](int i, int kt0, const Ring& b) {
@@ -237,19 +237,24 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
 #pragma unroll
     for (int u = 0; u < kDownTiles; ++u)
       if (kt0 + u < KT) {
-        const float4* hs = reinterpret_cast<const float4*>(hw + 128 * (kt0 + u) + 32 * g);
-        float hv[32];
+        const uint4* hs =
+            reinterpret_cast<const uint4*>(hw + (i & 1) * HSLOT + 128 * (kt0 + u) + 32 * g);
+        uint32_t hv[16];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float4 h4 = hs[v];
+        for (int v = 0; v < 4; ++v) {
+          const uint4 h4 = hs[v];
           hv[4 * v] = h4.x; hv[4 * v + 1] = h4.y; hv[4 * v + 2] = h4.z; hv[4 * v + 3] = h4.w;
         }
         const uint4 q = {b.q[u].x, b.q[u].y, b.q[u].z, b.q[u].w};
-        pe = fmaf(block_dot_f32(q, hv), e8m0_to_f32((b.sw >> (8 * u)) & 0xffu), pe);
+        pe = fmaf(block_dot_bf16(q, hv), e8m0_to_f32((b.sw >> (8 * u)) & 0xffu), pe);
       }
     acc = fmaf(gate[(size_t)t * k + wave + kDownWaves * i], pe, acc);
   };
   Ring ring[kDownDepth];
+  // the first two slots' h, then the first steps' weights
+  h_copy(0);
+  h_copy(1);
+  down_fence();
   static_for<kDownDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
   for (int it = 0; it < niter; ++it) {
     static_for<STEPS>([&](auto U) {
@@ -258,28 +263,23 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
       Ring& cur = ring[u % kDownDepth];
       Ring& fut = ring[(u + kDownDepth - 1) % kDownDepth];
       down_fence();
-      if constexpr (c == 0) {  // the slot's h: registers, then the wave's LDS region
-        v4u hr[HREGS];
-        h_load(i, 0, hr);
-        down_fence();
-        issue(s + kDownDepth - 1, fut);
-        down_fence();
-        down_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
-        down_fence();
-        h_store(0, hr);
-        static_for<HOPS / HREGS - 1>([&](auto Q) {  // f > 2048: the rest of h
-          h_load(i, Q() + 1, hr);
+      if constexpr (MULTI && c == 0) {
+        if (i > 0 && (i & 1) == 0) {  // slots i, i + 1: their h replaces the last two
+          h_copy(i);
+          h_copy(i + 1);
           down_fence();
-          down_wait_vmcnt<0>();
+          issue(s + kDownDepth - 1, fut);
           down_fence();
-          h_store(Q() + 1, hr);
-        });
-      } else {
-        issue(s + kDownDepth - 1, fut);
-        down_fence();
-        down_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads have landed
-        down_fence();
+          down_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
+          down_fence();
+          if (expert_of(i) >= 0) compute(i, 0, cur);
+          return;
+        }
       }
+      issue(s + kDownDepth - 1, fut);
+      down_fence();
+      down_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads (and before) landed
+      down_fence();
       if (expert_of(i) >= 0) compute(i, kDownTiles * c, cur);
     });
   }
@@ -297,44 +297,58 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
 }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const int32_t* idx, float* h32, hipStream_t st) {
+                              const int32_t* idx, uint16_t* hb, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
   hipLaunchKernelGGL(gemv_gateup_kernel, g1, dim3(256), 0, st, x, s.d, s.f, s.k, s.E, w.gate_q,
-                     w.gate_s, w.up_q, w.up_s, idx, h32);
+                     w.gate_s, w.up_q, w.up_s, idx, hb);
   return hipGetLastError();
 }
 
-template <int HOPS>
+static size_t down_lds_bytes(int nc) { return (size_t)kDownWaves * 2 * 1024 * nc; }
+
+template <int NC, bool MULTI>
 static hipError_t set_down_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel<HOPS>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kDownWaves * 1024 * HOPS);
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel<NC, MULTI>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds_bytes(NC));
+}
+
+template <int NC>
+static hipError_t set_down_lds_nc() {
+  hipError_t e = set_down_lds<NC, false>();
+  return e != hipSuccess ? e : set_down_lds<NC, true>();
 }
 
 hipError_t prepare_gemv(const Shape& s) {
-  switch (down_h_ops(s.f)) {
-    case 2: return set_down_lds<2>();
-    case 4: return set_down_lds<4>();
-    case 8: return set_down_lds<8>();
-    default: return set_down_lds<16>();
+  switch (down_chunks(s.f)) {
+    case 1: return set_down_lds_nc<1>();
+    case 2: return set_down_lds_nc<2>();
+    case 4: return set_down_lds_nc<4>();
+    default: return set_down_lds_nc<8>();
   }
 }
 
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
-                            const float* gate, const float* h32, float* y, hipStream_t st) {
+                            const float* gate, const uint16_t* hb, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(T, s.d / 16), block(64 * kDownWaves);
-  const int hops = down_h_ops(s.f);
-  const size_t lds = (size_t)kDownWaves * 1024 * hops;
-#define K3_DOWN(H)                                                                             \
-  hipLaunchKernelGGL(gemv_down_kernel<H>, grid, block, lds, st, s.d, s.f, s.k, s.E, w.down_q, \
-                     w.down_s, idx, gate, h32, y)
-  switch (hops) {
+  const int nc = down_chunks(s.f);
+  const bool multi = s.k > 2 * kDownWaves;
+  const size_t lds = down_lds_bytes(nc);
+#define K3_DOWN(NC)                                                                            \
+  do {                                                                                         \
+    if (multi)                                                                                 \
+      hipLaunchKernelGGL((gemv_down_kernel<NC, true>), grid, block, lds, st, s.d, s.f, s.k,   \
+                         s.E, w.down_q, w.down_s, idx, gate, hb, y);                           \
+    else                                                                                       \
+      hipLaunchKernelGGL((gemv_down_kernel<NC, false>), grid, block, lds, st, s.d, s.f, s.k,  \
+                         s.E, w.down_q, w.down_s, idx, gate, hb, y);                           \
+  } while (0)
+  switch (nc) {
+    case 1: K3_DOWN(1); break;
     case 2: K3_DOWN(2); break;
     case 4: K3_DOWN(4); break;
-    case 8: K3_DOWN(8); break;
-    default: K3_DOWN(16); break;
+    default: K3_DOWN(8); break;
   }
 #undef K3_DOWN
   return hipGetLastError();

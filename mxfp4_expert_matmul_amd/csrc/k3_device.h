@@ -18,6 +18,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 // E8M0 scale byte -> fp32 value 2^(b-127); 0 -> 2^-127 (subnormal); 255 -> NaN
 // (OCP Microscaling v1.0, E8M0).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {

@@ -73,12 +73,6 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 // arithmetic class as an fp32 dot product, at MFMA rate.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, size_t n,
                                                            uint16_t* __restrict__ w3) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {

@@ -136,12 +136,18 @@ def test_device_generator_matches_host(k3):
 # ----------------------------------------------------------------- small layers
 
 CUSTOM = synth.LayerConfig("ragged_d640_e16_k4_f384", 640, 16, 4, 384, 1, 11)
+# k = 40: a decode wave walks five slots (h re-staged every second slot);
+# f = 640 leaves a partial 4-tile chunk
+WIDE_K = synth.LayerConfig("wide_k_d256_e64_k40_f640", 256, 64, 40, 640, 1, 12)
+# f = 2304: the largest decode h staging (8 KB per slot) and a partial chunk
+WIDE_F = synth.LayerConfig("wide_f_d256_e16_k4_f2304", 256, 16, 4, 2304, 1, 13)
 
 
 @pytest.mark.parametrize("cfg,T", [
     (synth.CONFIGS[0], 1), (synth.CONFIGS[0], 3), (synth.CONFIGS[0], 5), (synth.CONFIGS[0], 130),
     (synth.CONFIGS[1], 1), (synth.CONFIGS[1], 4), (synth.CONFIGS[1], 9), (synth.CONFIGS[1], 256),
     (CUSTOM, 2), (CUSTOM, 77),
+    (WIDE_K, 1), (WIDE_K, 3), (WIDE_K, 40), (WIDE_F, 1), (WIDE_F, 2), (WIDE_F, 33),
 ])
 def test_layer_forward_small(k3, cfg, T):
     _say(f"case {cfg.name} T={T}")
