@@ -63,60 +63,141 @@ __device__ __forceinline__ float block_dot_f32(const uint4 q, const float* hv) {
   return acc;
 }
 
-// gate/up: one wave per (pair, 16-row tile of gate and of up). Lane (r, g)
-// takes row 16 rt + r, K block g of every 128-column tile, so one 16-byte
-// load per lane reads a whole 1 KB tile; its 32 activations are the same for
-// the 16 lanes of a group (a broadcast load). Rows are summed over the 4
-// groups at the end. Four K tiles per step share one scale dword per lane.
-// grid: (T*k pairs, ceil(f / 64)), block 256 (4 waves = 4 row tiles).
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Both GEMVs stream weights through rings of register sets filled by buffer
+// loads whose count per step is fixed, and wait on the load counter with
+// s_waitcnt vmcnt(N) (N = loads issued after the ones needed); the fences
+// keep the compiler from moving loads across those points.
+template <int N>
+__device__ __forceinline__ void gemv_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void gemv_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int V>
+using ic = std::integral_constant<int, V>;
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N - 1>{}): compile-time indices
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// gate/up: one wave per (pair, 16-row tile of gate and of up). The wave
+// first copies the token's x (bf16) into its own LDS region (buffer loads to
+// LDS), then walks K four 128-column tiles per step with the next
+// kGuDepth - 1 steps' weights in flight (ten buffer loads per step: four
+// 1 KB tiles of gate, four of up, one scale dword of each; past the last
+// tile they read zeros without touching memory). Lane (r, g) takes row
+// 16 rt + r, K block g of every tile, so one 16-byte load per lane reads a
+// whole 1 KB tile; its 32 activations are the same for the 16 lanes of a
+// group (an LDS broadcast). Rows are summed over the 4 groups at the end.
+// grid: (T*k pairs, ceil(f / 64)), block 256 (4 waves = 4 row tiles),
+// dynamic LDS 4 x XC KB.
+constexpr int kGuTiles = 4;
+constexpr int kGuDepth = 3;
+constexpr int kGuLoads = 2 * kGuTiles + 2;
+
+// 1 KB copies of x per wave (d <= 512 XC; lanes past d read zeros)
+__host__ __device__ constexpr int gu_x_copies(int d) {
+  return d <= 1024 ? 2 : d <= 2048 ? 4 : d <= 4096 ? 8 : d <= 7168 ? 14 : 16;
+}
+
+template <int XC>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ hb) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [4][512 * XC]
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int pair = blockIdx.x;
-  const int rt = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int rt = blockIdx.y * 4 + wave;
   const int RT = f >> 4, KT = d >> 7, KG = (KT + 3) >> 2;
-  if (rt >= RT) return;
+  if (rt >= RT) return;  // waves work independently (no barrier)
   const int t = pair / k;
   const int e = idx[pair];
   if (e < 0 || e >= E) return;  // dropped pair: never read downstream
-  const size_t tile0 = ((size_t)e * RT + rt) * KT;
-  const uint8_t* gqt = gq + tile0 * 1024 + 16 * lane;
-  const uint8_t* uqt = uq + tile0 * 1024 + 16 * lane;
-  const size_t grp0 = ((size_t)e * RT + rt) * KG;
-  const uint32_t* gst = reinterpret_cast<const uint32_t*>(gs + grp0 * 256) + lane;
-  const uint32_t* ust = reinterpret_cast<const uint32_t*>(us + grp0 * 256) + lane;
-  const uint16_t* xt = x + (size_t)t * d + 32 * g;
-  float ga = 0.0f, ua = 0.0f;
-  for (int kg = 0; kg < KG; ++kg) {
-    const uint32_t sgw = gst[64 * kg], suw = ust[64 * kg];
-    const int nk = min(4, KT - 4 * kg);
-    uint4 qg[4], qu[4];
-    uint32_t xr[4][16];
+  uint16_t* xw = xl + (size_t)wave * 512 * XC;
+  {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x + (size_t)t * d), 0, 2 * d, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < nk) {
-        const int kt = 4 * kg + j;
-        qg[j] = *reinterpret_cast<const uint4*>(gqt + (size_t)kt * 1024);
-        qu[j] = *reinterpret_cast<const uint4*>(uqt + (size_t)kt * 1024);
-        const uint4* xs = reinterpret_cast<const uint4*>(xt + 128 * kt);
+    for (int v = 0; v < XC; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_ptr)(xw + 512 * v), 16,
+                                               16 * lane + 1024 * v, 0, 0, 0);
+  }
+  // buffers over this row tile's K tiles (codes) and scale groups
+  const size_t row = (size_t)e * RT + rt;
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(gq + row * KT * 1024), 0, KT * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(uq + row * KT * 1024), 0, KT * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rgs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(gs + row * KG * 256), 0, KG * 256, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rus = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(us + row * KG * 256), 0, KG * 256, 0x00020000);
+  struct Ring {
+    v4u qg[kGuTiles], qu[kGuTiles];
+    uint32_t sg, su;
+  };
+  // step s: K tiles 4s .. 4s + 3 and their scale group s (offsets past the
+  // buffers read zeros)
+  auto issue = [&](int s, Ring& b) {
+#pragma unroll
+    for (int i = 0; i < kGuTiles; ++i) {
+      b.qg[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, 16 * lane + 1024 * (4 * s + i), 0, 0);
+      b.qu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, 16 * lane + 1024 * (4 * s + i), 0, 0);
+    }
+    b.sg = __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * lane + 256 * s, 0, 0);
+    b.su = __builtin_amdgcn_raw_buffer_load_b32(rus, 4 * lane + 256 * s, 0, 0);
+  };
+  float ga = 0.0f, ua = 0.0f;
+  auto compute = [&](int s, const Ring& b) {
+#pragma unroll
+    for (int i = 0; i < kGuTiles; ++i) {
+      const int kt = 4 * s + i;
+      if (kt < KT) {
+        const uint4* xs = reinterpret_cast<const uint4*>(xw + 128 * kt + 32 * g);
+        uint32_t xv[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const uint4 q = xs[v];
-          xr[j][4 * v] = q.x; xr[j][4 * v + 1] = q.y; xr[j][4 * v + 2] = q.z; xr[j][4 * v + 3] = q.w;
+          xv[4 * v] = q.x; xv[4 * v + 1] = q.y; xv[4 * v + 2] = q.z; xv[4 * v + 3] = q.w;
         }
+        const uint4 qg = {b.qg[i].x, b.qg[i].y, b.qg[i].z, b.qg[i].w};
+        const uint4 qu = {b.qu[i].x, b.qu[i].y, b.qu[i].z, b.qu[i].w};
+        ga = fmaf(block_dot_bf16(qg, xv), e8m0_to_f32((b.sg >> (8 * i)) & 0xffu), ga);
+        ua = fmaf(block_dot_bf16(qu, xv), e8m0_to_f32((b.su >> (8 * i)) & 0xffu), ua);
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < nk) {
-        ga = fmaf(block_dot_bf16(qg[j], xr[j]), e8m0_to_f32((sgw >> (8 * j)) & 0xffu), ga);
-        ua = fmaf(block_dot_bf16(qu[j], xr[j]), e8m0_to_f32((suw >> (8 * j)) & 0xffu), ua);
-      }
-    }
-  }
+  };
+  // K fully unrolled (XC >= KG steps), so the ring's register sets are fixed
+  // at compile time; steps past the last read zeros and compute nothing
+  Ring ring[kGuDepth];
+  gemv_fence();
+  static_for<kGuDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
+  static_for<XC>([&](auto S) {
+    constexpr int s = S();
+    gemv_fence();
+    if constexpr (s + kGuDepth - 1 < XC) issue(s + kGuDepth - 1, ring[(s + kGuDepth - 1) % kGuDepth]);
+    gemv_fence();
+    // step s's loads (and x, issued before all of them) have landed
+    constexpr int after = (XC - 1 - s < kGuDepth - 1 ? XC - 1 - s : kGuDepth - 1) * kGuLoads;
+    gemv_wait_vmcnt<after>();
+    gemv_fence();
+    if (4 * s < KT) compute(s, ring[s % kGuDepth]);
+  });
+  gemv_wait_vmcnt<0>();
   ga += __shfl_xor(ga, 16, 64);
   ga += __shfl_xor(ga, 32, 64);
   ua += __shfl_xor(ua, 16, 64);
@@ -145,33 +226,10 @@ constexpr int kDownTiles = 4;  // K tiles per step (a slot of f = 2048 takes 4 s
 constexpr int kDownWaves = 8;
 constexpr int kDownDepth = 4;  // ring of weight register sets
 constexpr int kDownLoads = kDownTiles + 1;
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // 4-tile chunks per slot (f <= 512 NC); a slot's bf16 h is NC KB
 __host__ __device__ constexpr int down_chunks(int f) {
   return f <= 512 ? 1 : f <= 1024 ? 2 : f <= 2048 ? 4 : 8;
-}
-
-template <int N>
-__device__ __forceinline__ void down_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void down_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-template <int V>
-using ic = std::integral_constant<int, V>;
-// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N - 1>{}): compile-time indices
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
-  (f(ic<I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // MULTI: a wave has more than two slots (k > 16), so h is copied again
@@ -254,7 +312,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
   // the first two slots' h, then the first steps' weights
   h_copy(0);
   h_copy(1);
-  down_fence();
+  gemv_fence();
   static_for<kDownDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
   for (int it = 0; it < niter; ++it) {
     static_for<STEPS>([&](auto U) {
@@ -262,28 +320,28 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
       const int s = it * STEPS + u, i = it * SPI + u / NC;
       Ring& cur = ring[u % kDownDepth];
       Ring& fut = ring[(u + kDownDepth - 1) % kDownDepth];
-      down_fence();
+      gemv_fence();
       if constexpr (MULTI && c == 0) {
         if (i > 0 && (i & 1) == 0) {  // slots i, i + 1: their h replaces the last two
           h_copy(i);
           h_copy(i + 1);
-          down_fence();
+          gemv_fence();
           issue(s + kDownDepth - 1, fut);
-          down_fence();
-          down_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
-          down_fence();
+          gemv_fence();
+          gemv_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
+          gemv_fence();
           if (expert_of(i) >= 0) compute(i, 0, cur);
           return;
         }
       }
       issue(s + kDownDepth - 1, fut);
-      down_fence();
-      down_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads (and before) landed
-      down_fence();
+      gemv_fence();
+      gemv_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads (and before) landed
+      gemv_fence();
       if (expert_of(i) >= 0) compute(i, kDownTiles * c, cur);
     });
   }
-  down_wait_vmcnt<0>();
+  gemv_wait_vmcnt<0>();
   acc += __shfl_xor(acc, 16, 64);
   acc += __shfl_xor(acc, 32, 64);
   if (g == 0) red[wave][r] = acc;
@@ -296,12 +354,24 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
   }
 }
 
+static size_t gateup_lds_bytes(int d) { return (size_t)4 * 1024 * gu_x_copies(d); }
+
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
                               const int32_t* idx, uint16_t* hb, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
-  hipLaunchKernelGGL(gemv_gateup_kernel, g1, dim3(256), 0, st, x, s.d, s.f, s.k, s.E, w.gate_q,
-                     w.gate_s, w.up_q, w.up_s, idx, hb);
+  const dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
+  const size_t lds = gateup_lds_bytes(s.d);
+#define K3_GATEUP(XC)                                                                          \
+  hipLaunchKernelGGL(gemv_gateup_kernel<XC>, g1, dim3(256), lds, st, x, s.d, s.f, s.k, s.E,    \
+                     w.gate_q, w.gate_s, w.up_q, w.up_s, idx, hb)
+  switch (gu_x_copies(s.d)) {
+    case 2: K3_GATEUP(2); break;
+    case 4: K3_GATEUP(4); break;
+    case 8: K3_GATEUP(8); break;
+    case 14: K3_GATEUP(14); break;
+    default: K3_GATEUP(16); break;
+  }
+#undef K3_GATEUP
   return hipGetLastError();
 }
 
@@ -320,6 +390,17 @@ static hipError_t set_down_lds_nc() {
 }
 
 hipError_t prepare_gemv(const Shape& s) {
+  const void* gu;
+  switch (gu_x_copies(s.d)) {
+    case 2: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<2>); break;
+    case 4: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<4>); break;
+    case 8: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<8>); break;
+    case 14: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<14>); break;
+    default: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<16>); break;
+  }
+  const hipError_t e = hipFuncSetAttribute(gu, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)gateup_lds_bytes(s.d));
+  if (e != hipSuccess) return e;
   switch (down_chunks(s.f)) {
     case 1: return set_down_lds_nc<1>();
     case 2: return set_down_lds_nc<2>();

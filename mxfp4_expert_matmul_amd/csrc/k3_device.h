@@ -28,9 +28,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // E8M0 scale byte -> fp32 value 2^(b-127); 0 -> 2^-127 (subnormal); 255 -> NaN
 // (OCP Microscaling v1.0, E8M0).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  if (b == 0u) return __uint_as_float(0x00400000u);
-  if (b == 255u) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(b << 23);
+  uint32_t u = b << 23;               // selects, not branches
+  u = (b == 0u) ? 0x00400000u : u;
+  u = (b == 255u) ? 0x7fc00000u : u;
+  return __uint_as_float(u);
 }
 
 // Butterfly sum over the 64 lanes of a wave; every lane gets the total.
