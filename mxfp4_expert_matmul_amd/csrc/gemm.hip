@@ -589,11 +589,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (i >= (size_t)T * d4) return;
   const int t = (int)(i / d4), c = (int)(i % d4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // every slot is read (a dropped pair's slot is allocated but unwritten and
+  // its value is replaced by zero, not multiplied), so the loads of several
+  // slots are in flight together
+#pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
-    if (e < 0 || e >= E) continue;
-    const float gw = gate[(size_t)t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(slots + ((size_t)t * k + j) * d)[c];
+    const bool on = e >= 0 && e < E;
+    const float gw = on ? gate[(size_t)t * k + j] : 0.0f;
+    float4 v = reinterpret_cast<const float4*>(slots + ((size_t)t * k + j) * d)[c];
+    if (!on) v = make_float4(0.f, 0.f, 0.f, 0.f);
     acc.x = fmaf(gw, v.x, acc.x);
     acc.y = fmaf(gw, v.y, acc.y);
     acc.z = fmaf(gw, v.z, acc.z);
