@@ -273,15 +273,10 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // Selection (top k keys in descending order) of one wave's V keys per lane.
-// The k-th largest of the 64 lane maxima is a lower bound tau of the k-th
-// largest key (k distinct keys reach it), so every selected key is >= tau.
+// The k-th largest of the 64 lane maxima is at most the k-th largest key (k
+// distinct keys reach it), and so is tau, its high word with a zero low
+// word: every selected key is >= tau.
 // Usually few keys pass; they are compacted into LDS and each one's rank
 // (the number of passing keys above it) is its position. If more than 64
 // pass, k rounds each take the largest key below the previous round's.
@@ -296,19 +291,17 @@ __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand,
   for (int w = 1; w < V; w *= 2)
 #pragma unroll
     for (int j = 0; j + w < V; j += 2 * w) m[j] = m[j + w] > m[j] ? m[j + w] : m[j];
-  // bitonic sort of the lane maxima, descending across the wave
-  uint64_t v = m[0];
+  // tau: the k-th largest high word (the ordered logit bits) of the lane
+  // maxima, built bit by bit from the top; a bit stays set when at least k
+  // lane maxima reach the prefix with it (a ballot count, no data exchange)
+  const uint32_t mh = (uint32_t)(m[0] >> 32);
+  uint32_t prefix = 0;
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-    for (int j = size >> 1; j > 0; j >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & size) == 0);
-      v = take_max ? (o > v ? o : v) : (o < v ? o : v);
-    }
-  const uint64_t tau =
-      ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), k - 1) << 32) |
-      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, k - 1);
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    if (__builtin_popcountll(__ballot(mh >= cand)) >= k) prefix = cand;
+  }
+  const uint64_t tau = (uint64_t)prefix << 32;
   // compact the keys >= tau (in lane order; their order does not matter)
   int c = 0;
 #pragma unroll
