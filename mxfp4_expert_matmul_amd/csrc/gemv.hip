@@ -9,8 +9,7 @@
 // each row over its four lane groups.
 //
 //   gemv_gateup: per (token, slot) pair and feature n:
-//       g = Wg[e][n,:] . x,  u = Wu[e][n,:] . x,  h[n] = SiLU(g) * u
-//       (fp32, stored rounded to bf16: relative error <= 2^-9)
+//       g = Wg[e][n,:] . x,  u = Wu[e][n,:] . x,  h[n] = SiLU(g) * u   (fp32)
 //   gemv_down:   per token and output row m:
 //       y[m] = sum_j gate_j * (Wd[e_j][m,:] . h_j)                        (fp32)
 // Both are deterministic (fixed summation order, no atomics).
@@ -115,7 +114,7 @@ template <int XC>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ hb) {
+    const int32_t* __restrict__ idx, float* __restrict__ h32) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [4][512 * XC]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,72 +201,75 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   ga += __shfl_xor(ga, 32, 64);
   ua += __shfl_xor(ua, 16, 64);
   ua += __shfl_xor(ua, 32, 64);
-  if (g == 0) hb[(size_t)pair * f + 16 * rt + r] = f32_to_bf16_rne(silu_f32(ga) * ua);
+  if (g == 0) h32[(size_t)pair * f + 16 * rt + r] = silu_f32(ga) * ua;
 }
 
-// down + combine: workgroup = one token x one 16-row tile of the output; its
-// 8 waves split the token's k slots (wave w: j = w, w + 8, ...). A wave walks
-// its (slot, 4-tile chunk) steps with the weights of the next kDownDepth - 1
-// steps in flight while it computes the current one (a ring of register
-// sets). Every step issues the same five buffer loads (four 1 KB tiles and
-// one scale dword per lane); a load past the row tile's K extent, of a
-// dropped slot or past the wave's last slot is given an empty buffer and
-// reads zeros without touching memory (the whole offset is in the per-lane
-// part, which the buffer's size check covers), so every step issues the same
-// loads and the counted waits below are exact. The h (bf16) of two slots at
-// a time is copied straight into the wave's own LDS region (buffer loads to
-// LDS); with k <= 16 that happens once, before the first weights, so no step
-// waits for h. Each 32-value block of h is read back as a broadcast. Lane
-// (r, g) keeps a gate-weighted partial of row 16 rt + r over K block g of
-// every tile; partials meet across lane groups, then across waves in fixed
-// order. Deterministic, no atomics.
-// grid: (T, d / 16), block 512, dynamic LDS 8 waves x 2 slots x NC KB.
-constexpr int kDownTiles = 4;  // K tiles per step (a slot of f = 2048 takes 4 steps)
-constexpr int kDownWaves = 8;
+// down + combine: workgroup = one token x two 16-row tiles of the output; its
+// 16 waves take one slot each (wave w: j = w, w + 16, ...). A wave copies its
+// slot's h (fp32, up to 2048 values: one "piece" of K) straight into its own
+// LDS region (buffer loads to LDS) and then walks 4-tile steps over both row
+// tiles with the weights of the next kDownDepth - 1 steps in flight (a ring
+// of register sets). Every step issues the same five buffer loads (four 1 KB
+// tiles and one scale dword per lane); a load past the row tile's K extent
+// or of a dropped slot is given an empty buffer and reads zeros without
+// touching memory (the whole offset is in the per-lane part, which the
+// buffer's size check covers), so the counted waits below are exact. With
+// k <= 16 and f <= 2048 the h copy is the wave's first load and no step
+// waits for it; otherwise h is copied again at every (slot, piece) segment.
+// Each 32-value block of h is read back as an LDS broadcast. Lane (r, g)
+// keeps gate-weighted partials of rows 16 rt + r over K block g of every
+// tile; partials meet across lane groups, then across waves in fixed order.
+// Deterministic, no atomics.
+// grid: (T, d / 32), block 1024, dynamic LDS 16 waves x 2 KB x NCP.
+constexpr int kDownTiles = 4;  // K tiles per step
+constexpr int kDownWaves = 16;
 constexpr int kDownDepth = 4;  // ring of weight register sets
 constexpr int kDownLoads = kDownTiles + 1;
+constexpr int kDownPiece = 2048;  // h values staged at once per wave (8 KB)
 
-// 4-tile chunks per slot (f <= 512 NC); a slot's bf16 h is NC KB
-__host__ __device__ constexpr int down_chunks(int f) {
-  return f <= 512 ? 1 : f <= 1024 ? 2 : f <= 2048 ? 4 : 8;
+// 4-tile chunks per h piece (a piece is min(f, 2048) values, <= 512 NCP)
+__host__ __device__ constexpr int down_piece_chunks(int f) {
+  return f <= 512 ? 1 : f <= 1024 ? 2 : 4;
 }
 
-// MULTI: a wave has more than two slots (k > 16), so h is copied again
-// every second slot
-template <int NC, bool MULTI>
+// MULTI: more than one (slot, piece) segment per wave (k > 16 or f > 2048)
+template <int NCP, bool MULTI>
 __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
     int d, int f, int k, int E, const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
-    const uint16_t* __restrict__ hb, float* __restrict__ y) {
-  constexpr int SPI = NC >= kDownDepth ? 1 : kDownDepth / NC;  // slots per loop iteration
-  constexpr int STEPS = SPI * NC;
-  static_assert(STEPS % kDownDepth == 0, "ring phase must repeat every iteration");
-  constexpr int HSLOT = 512 * NC;  // bf16 values of one slot's LDS region
-  extern __shared__ __attribute__((aligned(16))) uint16_t hl[];  // [kDownWaves][2][HSLOT]
-  __shared__ float red[kDownWaves][16];
+    const float* __restrict__ h32, float* __restrict__ y) {
+  constexpr int SPS = 2 * NCP;                                 // steps per segment
+  constexpr int DEPTH = SPS < kDownDepth ? SPS : kDownDepth;  // ring depth
+  static_assert(SPS % DEPTH == 0, "ring phase must repeat every segment");
+  constexpr int HP = 512 * NCP;  // h values per piece (= LDS floats per wave)
+  extern __shared__ __attribute__((aligned(16))) float hl[];  // [kDownWaves][HP]
+  __shared__ float red[kDownWaves][32];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int t = blockIdx.x, rt = blockIdx.y;
+  const int t = blockIdx.x, rp = blockIdx.y;  // row tiles 2 rp, 2 rp + 1
   const int RT = d >> 4, KT = f >> 7, KG = (KT + 3) >> 2;
-  uint16_t* hw = hl + (size_t)wave * 2 * HSLOT;
+  const int npiece = (f + kDownPiece - 1) / kDownPiece;
+  float* hw = hl + (size_t)wave * HP;
   struct Ring {
     v4u q[kDownTiles];
     uint32_t sw;
   };
-  const int nslot = (k - wave + kDownWaves - 1) / kDownWaves;  // slots wave, wave + 8, ...
-  const int niter = (nslot + SPI - 1) / SPI;
+  const int nslot = (k - wave + kDownWaves - 1) / kDownWaves;  // slots wave, wave + 16, ...
+  const int nseg = nslot * npiece;
   // expert of the wave's i-th slot, -1 past the last slot or for a dropped pair
   auto expert_of = [&](int i) {
     if (i >= nslot) return -1;
     const int e = idx[(size_t)t * k + wave + kDownWaves * i];
     return (e >= 0 && e < E) ? e : -1;
   };
-  // the five loads of step s (slot s / NC, K tiles from 4 (s % NC))
-  auto issue = [&](int s, Ring& b) {
-    const int e = expert_of(s / NC), kt0 = kDownTiles * (s % NC);
+  // step u of segment sg: row tile 2 rp + u / NCP, K tiles from
+  // 16 piece + 4 (u % NCP) (a piece is 16 K tiles)
+  auto issue = [&](int sg, int u, Ring& b) {
+    const int e = sg < nseg ? expert_of(sg / npiece) : -1;
+    const int kt0 = (kDownPiece / 128) * (sg % npiece) + kDownTiles * (u % NCP);
     const bool on = e >= 0;
-    const size_t row = on ? (size_t)e * RT + rt : 0;
+    const size_t row = on ? (size_t)e * RT + 2 * rp + u / NCP : 0;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(dq + row * KT * 1024), 0, on ? KT * 1024 : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -277,93 +279,104 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
       b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane + 1024 * (kt0 + i), 0, 0);
     b.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane + 256 * (kt0 >> 2), 0, 0);
   };
-  // h of the wave's i-th slot -> its LDS region (NC copies of 1 KB; values
-  // past f, and slots with nothing to compute, read as zeros)
-  auto h_copy = [&](int i) {
-    const bool on = expert_of(i) >= 0;
-    const size_t pair = on ? (size_t)t * k + wave + kDownWaves * i : 0;
+  // h piece of segment sg -> the wave's LDS region (2 NCP copies of 1 KB;
+  // values past f, and segments with nothing to compute, read as zeros)
+  auto h_copy = [&](int sg) {
+    const bool on = sg < nseg && expert_of(sg / npiece) >= 0;
+    const size_t pair = on ? (size_t)t * k + wave + kDownWaves * (sg / npiece) : 0;
+    const int p0 = kDownPiece * (sg % npiece);
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(hb + pair * f), 0, on ? 2 * f : 0, 0x00020000);
+        const_cast<float*>(h32 + pair * f + (on ? p0 : 0)), 0, on ? 4 * (f - p0) : 0, 0x00020000);
 #pragma unroll
-    for (int v = 0; v < NC; ++v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_ptr)(hw + (i & 1) * HSLOT + 512 * v),
-                                               16, 16 * lane + 1024 * v, 0, 0, 0);
+    for (int v = 0; v < 2 * NCP; ++v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_ptr)(hw + 256 * v), 16,
+                                               16 * lane + 1024 * v, 0, 0, 0);
   };
-  float acc = 0.0f;
-  auto compute = [&](int i, int kt0, const Ring& b) {
+  float acc0 = 0.0f, acc1 = 0.0f;  // rows of row tile 2 rp and 2 rp + 1
+  auto compute = [&](int sg, int u, const Ring& b) {
+    const int c = u % NCP;
+    const int kt0 = (kDownPiece / 128) * (sg % npiece) + kDownTiles * c;
     float pe = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kDownTiles; ++u)
-      if (kt0 + u < KT) {
-        const uint4* hs =
-            reinterpret_cast<const uint4*>(hw + (i & 1) * HSLOT + 128 * (kt0 + u) + 32 * g);
-        uint32_t hv[16];
+    for (int i = 0; i < kDownTiles; ++i)
+      if (kt0 + i < KT) {
+        const float4* hs = reinterpret_cast<const float4*>(hw + 128 * (kDownTiles * c + i) + 32 * g);
+        float hv[32];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 h4 = hs[v];
+        for (int v = 0; v < 8; ++v) {
+          const float4 h4 = hs[v];
           hv[4 * v] = h4.x; hv[4 * v + 1] = h4.y; hv[4 * v + 2] = h4.z; hv[4 * v + 3] = h4.w;
         }
-        const uint4 q = {b.q[u].x, b.q[u].y, b.q[u].z, b.q[u].w};
-        pe = fmaf(block_dot_bf16(q, hv), e8m0_to_f32((b.sw >> (8 * u)) & 0xffu), pe);
+        const uint4 q = {b.q[i].x, b.q[i].y, b.q[i].z, b.q[i].w};
+        pe = fmaf(block_dot_f32(q, hv), e8m0_to_f32((b.sw >> (8 * i)) & 0xffu), pe);
       }
-    acc = fmaf(gate[(size_t)t * k + wave + kDownWaves * i], pe, acc);
+    const float gw = gate[(size_t)t * k + wave + kDownWaves * (sg / npiece)];
+    if (u < NCP)
+      acc0 = fmaf(gw, pe, acc0);
+    else
+      acc1 = fmaf(gw, pe, acc1);
   };
-  Ring ring[kDownDepth];
-  // the first two slots' h, then the first steps' weights
-  h_copy(0);
-  h_copy(1);
-  gemv_fence();
-  static_for<kDownDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
-  for (int it = 0; it < niter; ++it) {
-    static_for<STEPS>([&](auto U) {
-      constexpr int u = U(), c = u % NC;
-      const int s = it * STEPS + u, i = it * SPI + u / NC;
-      Ring& cur = ring[u % kDownDepth];
-      Ring& fut = ring[(u + kDownDepth - 1) % kDownDepth];
+  Ring ring[DEPTH];
+  // one segment's steps; its first DEPTH - 1 steps' weights are in flight on
+  // entry, and on exit the next segment's first DEPTH - 1 are
+  auto segment = [&](int sg) {
+    static_for<SPS>([&](auto U) {
+      constexpr int u = U();
+      constexpr int un = u + DEPTH - 1;  // step issued now: un of sg, or un - SPS of sg + 1
       gemv_fence();
-      if constexpr (MULTI && c == 0) {
-        if (i > 0 && (i & 1) == 0) {  // slots i, i + 1: their h replaces the last two
-          h_copy(i);
-          h_copy(i + 1);
-          gemv_fence();
-          issue(s + kDownDepth - 1, fut);
-          gemv_fence();
-          gemv_wait_vmcnt<kDownLoads>();  // h, and everything issued before it, has landed
-          gemv_fence();
-          if (expert_of(i) >= 0) compute(i, 0, cur);
-          return;
-        }
-      }
-      issue(s + kDownDepth - 1, fut);
+      if constexpr (un < SPS)
+        issue(sg, un, ring[un % DEPTH]);
+      else
+        issue(sg + 1, un - SPS, ring[un % DEPTH]);
       gemv_fence();
-      gemv_wait_vmcnt<kDownLoads * (kDownDepth - 1)>();  // step s's loads (and before) landed
+      gemv_wait_vmcnt<kDownLoads * (DEPTH - 1)>();  // step u's loads (and before) landed
       gemv_fence();
-      if (expert_of(i) >= 0) compute(i, kDownTiles * c, cur);
+      if (expert_of(sg / npiece) >= 0) compute(sg, u, ring[u % DEPTH]);
     });
+  };
+  // the first segment's h, then its first steps' weights
+  h_copy(0);
+  gemv_fence();
+  static_for<DEPTH - 1>([&](auto P) { issue(0, P(), ring[P()]); });
+  segment(0);
+  if constexpr (MULTI) {
+    for (int sg = 1; sg < nseg; ++sg) {
+      gemv_fence();
+      h_copy(sg);  // every LDS read of the previous segment has completed
+      gemv_fence();
+      gemv_wait_vmcnt<0>();
+      gemv_fence();
+      segment(sg);
+    }
   }
   gemv_wait_vmcnt<0>();
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
-  if (g == 0) red[wave][r] = acc;
+  acc0 += __shfl_xor(acc0, 16, 64);
+  acc0 += __shfl_xor(acc0, 32, 64);
+  acc1 += __shfl_xor(acc1, 16, 64);
+  acc1 += __shfl_xor(acc1, 32, 64);
+  if (g == 0) {
+    red[wave][r] = acc0;
+    red[wave][16 + r] = acc1;
+  }
   __syncthreads();
-  if (tid < 16) {
+  if (tid < 32) {
     float s = red[0][tid];
 #pragma unroll
     for (int w = 1; w < kDownWaves; ++w) s += red[w][tid];
-    y[(size_t)t * d + 16 * rt + tid] = s;
+    y[(size_t)t * d + 32 * rp + tid] = s;
   }
 }
 
 static size_t gateup_lds_bytes(int d) { return (size_t)4 * 1024 * gu_x_copies(d); }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const int32_t* idx, uint16_t* hb, hipStream_t st) {
+                              const int32_t* idx, float* h32, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
   const size_t lds = gateup_lds_bytes(s.d);
 #define K3_GATEUP(XC)                                                                          \
   hipLaunchKernelGGL(gemv_gateup_kernel<XC>, g1, dim3(256), lds, st, x, s.d, s.f, s.k, s.E,    \
-                     w.gate_q, w.gate_s, w.up_q, w.up_s, idx, hb)
+                     w.gate_q, w.gate_s, w.up_q, w.up_s, idx, h32)
   switch (gu_x_copies(s.d)) {
     case 2: K3_GATEUP(2); break;
     case 4: K3_GATEUP(4); break;
@@ -375,18 +388,18 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
   return hipGetLastError();
 }
 
-static size_t down_lds_bytes(int nc) { return (size_t)kDownWaves * 2 * 1024 * nc; }
+static size_t down_lds_bytes(int ncp) { return (size_t)kDownWaves * 2048 * ncp; }
 
-template <int NC, bool MULTI>
+template <int NCP, bool MULTI>
 static hipError_t set_down_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel<NC, MULTI>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds_bytes(NC));
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_down_kernel<NCP, MULTI>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds_bytes(NCP));
 }
 
-template <int NC>
+template <int NCP>
 static hipError_t set_down_lds_nc() {
-  hipError_t e = set_down_lds<NC, false>();
-  return e != hipSuccess ? e : set_down_lds<NC, true>();
+  hipError_t e = set_down_lds<NCP, false>();
+  return e != hipSuccess ? e : set_down_lds<NCP, true>();
 }
 
 hipError_t prepare_gemv(const Shape& s) {
@@ -401,35 +414,33 @@ hipError_t prepare_gemv(const Shape& s) {
   const hipError_t e = hipFuncSetAttribute(gu, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)gateup_lds_bytes(s.d));
   if (e != hipSuccess) return e;
-  switch (down_chunks(s.f)) {
+  switch (down_piece_chunks(s.f)) {
     case 1: return set_down_lds_nc<1>();
     case 2: return set_down_lds_nc<2>();
-    case 4: return set_down_lds_nc<4>();
-    default: return set_down_lds_nc<8>();
+    default: return set_down_lds_nc<4>();
   }
 }
 
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
-                            const float* gate, const uint16_t* hb, float* y, hipStream_t st) {
+                            const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid(T, s.d / 16), block(64 * kDownWaves);
-  const int nc = down_chunks(s.f);
-  const bool multi = s.k > 2 * kDownWaves;
-  const size_t lds = down_lds_bytes(nc);
-#define K3_DOWN(NC)                                                                            \
+  const dim3 grid(T, s.d / 32), block(64 * kDownWaves);
+  const int ncp = down_piece_chunks(s.f);
+  const bool multi = s.k > kDownWaves || s.f > kDownPiece;
+  const size_t lds = down_lds_bytes(ncp);
+#define K3_DOWN(NCP)                                                                           \
   do {                                                                                         \
     if (multi)                                                                                 \
-      hipLaunchKernelGGL((gemv_down_kernel<NC, true>), grid, block, lds, st, s.d, s.f, s.k,   \
-                         s.E, w.down_q, w.down_s, idx, gate, hb, y);                           \
+      hipLaunchKernelGGL((gemv_down_kernel<NCP, true>), grid, block, lds, st, s.d, s.f, s.k,  \
+                         s.E, w.down_q, w.down_s, idx, gate, h32, y);                          \
     else                                                                                       \
-      hipLaunchKernelGGL((gemv_down_kernel<NC, false>), grid, block, lds, st, s.d, s.f, s.k,  \
-                         s.E, w.down_q, w.down_s, idx, gate, hb, y);                           \
+      hipLaunchKernelGGL((gemv_down_kernel<NCP, false>), grid, block, lds, st, s.d, s.f, s.k, \
+                         s.E, w.down_q, w.down_s, idx, gate, h32, y);                          \
   } while (0)
-  switch (nc) {
+  switch (ncp) {
     case 1: K3_DOWN(1); break;
     case 2: K3_DOWN(2); break;
-    case 4: K3_DOWN(4); break;
-    default: K3_DOWN(8); break;
+    default: K3_DOWN(4); break;
   }
 #undef K3_DOWN
   return hipGetLastError();

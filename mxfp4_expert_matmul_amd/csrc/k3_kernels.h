@@ -48,9 +48,9 @@ hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* coun
 
 // gemv.hip (decode path, T <= kGemvMaxT)
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const int32_t* idx, uint16_t* hb, hipStream_t st);
+                              const int32_t* idx, float* h32, hipStream_t st);
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
-                            const float* gate, const uint16_t* hb, float* y, hipStream_t st);
+                            const float* gate, const float* h32, float* y, hipStream_t st);
 // once per handle: raise the dynamic LDS limit the decode down kernel needs
 hipError_t prepare_gemv(const Shape& s);
 

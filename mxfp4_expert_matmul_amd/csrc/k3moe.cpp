@@ -27,7 +27,7 @@ inline bool aligned(const void* p, size_t a) {
 
 // Byte offsets of every workspace buffer for one config.
 struct Plan {
-  size_t logits, idx, gate, counts, offsets, perm, bhist, tiles, ntiles, xq, xs, hq, hs, hb,
+  size_t logits, idx, gate, counts, offsets, perm, bhist, tiles, ntiles, xq, xs, hq, hs, h32,
       slots, wr3;
   size_t total;
   int max_tiles;
@@ -81,7 +81,7 @@ Plan make_plan(const k3moe_config* c) {
   p.xs = take(2 * T * (d / 32));
   p.hq = take(2 * P * f);
   p.hs = take(2 * P * (f / 32));
-  p.hb = take(tg * k * f * 2);
+  p.h32 = take(tg * k * f * 4);
   p.slots = take(P * d * 4);
   p.wr3 = take(3 * E * d * 2);
   p.total = o;
@@ -124,7 +124,7 @@ struct k3moe {
   uint8_t* xs;
   uint8_t* hq;
   uint8_t* hs;
-  uint16_t* hb;  // decode: SwiGLU output per pair, bf16
+  float* h32;  // decode: SwiGLU output per pair
   float* slots;
   uint16_t* wr3;  // router weights as three bf16 terms, derived at create
   // stage timing (k3moe_profile_begin / k3moe_profile_end)
@@ -193,10 +193,10 @@ int run_experts(k3moe* h, const uint16_t* x, int T, const int32_t* idx, const fl
   hipError_t e;
   if (T <= k3::kGemvMaxT) {
     e = stage(h, K3MOE_STAGE_GATEUP, st,
-              [&] { return k3::launch_gemv_gateup(x, T, s, w, idx, h->hb, st); });
+              [&] { return k3::launch_gemv_gateup(x, T, s, w, idx, h->h32, st); });
     if (e != hipSuccess) return K3MOE_EHIP;
     e = stage(h, K3MOE_STAGE_DOWN, st,
-              [&] { return k3::launch_gemv_down(T, s, w, idx, gate, h->hb, y, st); });
+              [&] { return k3::launch_gemv_down(T, s, w, idx, gate, h->h32, y, st); });
     return hip_status(e);
   }
   e = stage(h, K3MOE_STAGE_GROUP, st, [&] {
@@ -312,7 +312,7 @@ int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3
   h->xs = h->ws + plan.xs;
   h->hq = h->ws + plan.hq;
   h->hs = h->ws + plan.hs;
-  h->hb = reinterpret_cast<uint16_t*>(h->ws + plan.hb);
+  h->h32 = reinterpret_cast<float*>(h->ws + plan.h32);
   h->slots = reinterpret_cast<float*>(h->ws + plan.slots);
   h->wr3 = reinterpret_cast<uint16_t*>(h->ws + plan.wr3);
   if (k3::prepare_gemv(shape_of(h)) != hipSuccess ||
