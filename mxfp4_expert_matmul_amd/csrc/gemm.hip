@@ -168,24 +168,23 @@ struct GemmShape {
   static constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // output rows per workgroup
 };
 
-// Loads (vector-memory instructions) one wave issues per K tile, in order:
-// kActOps activation copies (kActGroups row groups + 1 scale copy), then
-// kWOps weight tiles, then for every fourth tile kWOps scale dwords (for the
-// next 4 tiles). The order is pinned (compiler barriers around each group).
+// Loads (vector-memory instructions) one wave issues in the step that
+// computes tile c, in order: kActOps activation copies of tile c + 1
+// (kActGroups row groups + 1 scale copy), then kWOps weight tiles of tile
+// c + kWStages - 1, then, when that tile starts a group of 4, kWOps scale
+// dwords for the group. The order is pinned (compiler barriers around each
+// group).
 constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 terms, 4 waves)
 constexpr int kScRows = 128;  // scale rows per term in LDS: two waves copy 64 each (rows past
                               // the tile's tokens read nothing)
 constexpr int kActOps = kActGroups + 1;
 constexpr int kWOps = 4;  // NM * NRT for both modes
-// Loads issued after the last activation copy of tile c, counted at the top
-// of the step that computes tile c (P = c % 4): tile c's weights, and the
-// scale dwords of c's group of 4 tiles when c starts one (they go out right
-// after). Copies complete in issue order with the other loads, so waiting
+// Counted at the top of the step that computes tile c (P = c % 8): tile c's
+// copies went out one step earlier, followed only by the weights of tile
+// c + kWStages - 2 (and their group's scale dwords when that tile starts a
+// group). Copies complete in issue order with the other loads, so waiting
 // for the counter to drop to this value means the wave's copies of tile c
-// have landed in LDS.
-// Tile c's copies go out one step before the step that computes it,
-// followed by the weights of tile c + kWStages - 1 (and their group's scale
-// dwords when that tile starts a group of 4).
+// have landed in LDS; tile c's own weights, issued before them, have too.
 template <int P>
 constexpr int loads_after_act() {
   return kWOps + (((P + kWStages - 2) & 3) == 0 ? kWOps : 0);
