@@ -435,3 +435,31 @@ def test_k3_prefill_4096_skewed(k3, big_layers):
     tokens = np.unique(np.concatenate([hot_tokens[:2], [cfg.T - 1], rng.choice(cfg.T, 1)]))
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
                    label="k3 prefill 4096 skew")
+
+
+@pytest.mark.timeout(900)
+def test_k3_prefill_max_tokens(k3, big_layers):
+    """The largest T the K3 shape accepts (T*k*f = 2^30: 32768 tokens, 524288
+    pairs): every offset of the grouped path at its widest. Routing is checked
+    for every token, outputs for tokens of the hottest expert, the first and
+    the last token."""
+    st = big_layers(4, 4096)
+    cfg = st["cfg"]
+    T = (1 << 30) // (cfg.k * cfg.f)
+    _say(f"case k3 prefill max tokens T={T}")
+    layer = _layer(k3, cfg, st["dw"], T)
+    x = synth.gen_x(cfg, T=T)
+    logits = oracle.router_logits(x, st["wr"], st["bias"])
+    ridx, _ = oracle.topk_gates(logits, cfg.k)
+    del logits
+    counts = np.bincount(ridx.reshape(-1), minlength=cfg.E)
+    hot = int(np.argmax(counts))
+    _say(f"hottest expert {hot} with {counts[hot]} tokens")
+    hot_tokens = np.nonzero(np.any(ridx == hot, axis=1))[0]
+    tokens = np.unique(np.concatenate([[0, T - 1], hot_tokens[[0, -1]]]))
+    try:
+        _run_and_check(k3, layer, cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
+                       label=f"k3 prefill T={T}")
+    finally:
+        layer.close()
+        torch.cuda.empty_cache()
