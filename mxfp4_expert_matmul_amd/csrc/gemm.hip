@@ -35,6 +35,7 @@ namespace k3 {
 
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
+constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed (nt)
 
 // ------------------------------------------------------------- split of x
 // One thread per 32-element block of x.
@@ -312,7 +313,9 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // every wave issues the same loads.
   // Weight loads go through a buffer over the wave's NRT row tiles, so the
   // ring's look-ahead past the last K tile reads nothing (an offset past the
-  // buffer returns zeros without a memory access).
+  // buffer returns zeros without a memory access). Weights are read once:
+  // they are loaded non-temporal so they do not evict the activations, which
+  // every row block of the tile reads again, from the L2.
   const int rt0 = (wave_on ? w0 : 0) >> 4;
   constexpr uint32_t kNoRead = 0x7fff0000u;  // beyond any buffer here (all < 2^31 - 2^16)
   __amdgpu_buffer_rsrc_t wq_rs[NM];
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       for (int rt = 0; rt < NRT; ++rt)
         ws.q[m][rt] = __builtin_bit_cast(
             v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                     wq_rs[m], kt < KT ? 16 * lane + (rt * KT + kt) * 1024 : (int)kNoRead, 0, 0));
+                     wq_rs[m], kt < KT ? 16 * lane + (rt * KT + kt) * 1024 : (int)kNoRead, 0, kNonTemporal));
   };
   // scale dwords of groups of 4 K tiles: even groups in sa, odd groups in sb
   // (two named sets, each live across the loop, so no copy is needed)
@@ -561,7 +564,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     }
   } else {
     // this pair's expert output, rows w0 + 16 rt + 4 g + q of token column r,
-    // stored in the pair's own slot (no atomics; summed per token later)
+    // stored in the pair's own slot (no atomics; summed per token later;
+    // streamed past the caches, it is read once by the combine)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (ct >= nct) continue;
@@ -571,8 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       float* o = slots + (size_t)pair * nrows + w0 + 4 * g;
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
-        *reinterpret_cast<float4*>(o + 16 * rt) =
-            make_float4(acc[0][rt][ct][0], acc[0][rt][ct][1], acc[0][rt][ct][2], acc[0][rt][ct][3]);
+        __builtin_nontemporal_store(acc[0][rt][ct], reinterpret_cast<v4f*>(o + 16 * rt));
     }
   }
 }
@@ -596,7 +599,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int e = idx[(size_t)t * k + j];
     const bool on = e >= 0 && e < E;
     const float gw = on ? gate[(size_t)t * k + j] : 0.0f;
-    float4 v = reinterpret_cast<const float4*>(slots + ((size_t)t * k + j) * d)[c];
+    const v4f vv =
+        __builtin_nontemporal_load(reinterpret_cast<const v4f*>(slots + ((size_t)t * k + j) * d) + c);
+    float4 v = make_float4(vv[0], vv[1], vv[2], vv[3]);
     if (!on) v = make_float4(0.f, 0.f, 0.f, 0.f);
     acc.x = fmaf(gw, v.x, acc.x);
     acc.y = fmaf(gw, v.y, acc.y);

@@ -64,6 +64,10 @@ __device__ __forceinline__ float block_dot_f32(const uint4 q, const float* hv) {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// Expert weights are read once per call: their buffer loads are streamed
+// (non-temporal), so they do not push the router weights and activations out
+// of the caches.
+constexpr int kNonTemporal = 2;
 
 // Both GEMVs stream weights through rings of register sets filled by buffer
 // loads whose count per step is fixed, and wait on the load counter with
@@ -154,8 +158,8 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   auto issue = [&](int s, Ring& b) {
 #pragma unroll
     for (int i = 0; i < kGuTiles; ++i) {
-      b.qg[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, 16 * lane + 1024 * (4 * s + i), 0, 0);
-      b.qu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, 16 * lane + 1024 * (4 * s + i), 0, 0);
+      b.qg[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, 16 * lane + 1024 * (4 * s + i), 0, kNonTemporal);
+      b.qu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, 16 * lane + 1024 * (4 * s + i), 0, kNonTemporal);
     }
     b.sg = __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * lane + 256 * s, 0, 0);
     b.su = __builtin_amdgcn_raw_buffer_load_b32(rus, 4 * lane + 256 * s, 0, 0);
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
         const_cast<uint8_t*>(ds + row * KG * 256), 0, on ? KG * 256 : 0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kDownTiles; ++i)
-      b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane + 1024 * (kt0 + i), 0, 0);
+      b.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane + 1024 * (kt0 + i), 0, kNonTemporal);
     b.sw = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane + 256 * (kt0 >> 2), 0, 0);
   };
   // h piece of segment sg -> the wave's LDS region (2 NCP copies of 1 KB;
