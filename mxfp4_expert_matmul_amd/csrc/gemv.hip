@@ -18,6 +18,7 @@
 
 #include "k3_device.h"
 #include "k3_kernels.h"
+#include "topk_device.h"
 
 namespace k3 {
 
@@ -103,6 +104,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // 16 rt + r, K block g of every tile, so one 16-byte load per lane reads a
 // whole 1 KB tile; its 32 activations are the same for the 16 lanes of a
 // group (an LDS broadcast). Rows are summed over the 4 groups at the end.
+// With `logits` given (the whole-layer call), each wave first selects its
+// token's top k itself (the same selection as the top-k kernel, no workgroup
+// sync) and takes its pair's expert from it, so no top-k launch sits between
+// the router and this kernel; the workgroup of slot 0 and row block 0
+// writes the token's idx and gates for the down GEMV and the caller.
+// Otherwise idx is the caller's routing.
 // grid: (T*k pairs, ceil(f / 64)), block 256 (4 waves = 4 row tiles),
 // dynamic LDS 4 x XC KB.
 constexpr int kGuTiles = 4;
@@ -114,12 +121,15 @@ __host__ __device__ constexpr int gu_x_copies(int d) {
   return d <= 1024 ? 2 : d <= 2048 ? 4 : d <= 4096 ? 8 : d <= 7168 ? 14 : 16;
 }
 
-template <int XC>
+template <int XC, int V>  // V: logits per lane in the selection, E <= 64 V
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
-    const int32_t* __restrict__ idx, float* __restrict__ h32) {
+    const float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate,
+    float* __restrict__ h32) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [4][512 * XC]
+  __shared__ uint64_t cand[4][64];
+  __shared__ uint64_t sel[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -127,17 +137,30 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   const int rt = blockIdx.y * 4 + wave;
   const int RT = f >> 4, KT = d >> 7, KG = (KT + 3) >> 2;
   if (rt >= RT) return;  // waves work independently (no barrier)
-  const int t = pair / k;
-  const int e = idx[pair];
-  if (e < 0 || e >= E) return;  // dropped pair: never read downstream
+  const int t = pair / k, j = pair - t * k;
   uint16_t* xw = xl + (size_t)wave * 512 * XC;
-  {
+  {  // x first: its copy does not depend on the expert
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(x + (size_t)t * d), 0, 2 * d, 0x00020000);
 #pragma unroll
     for (int v = 0; v < XC; ++v)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_ptr)(xw + 512 * v), 16,
                                                16 * lane + 1024 * v, 0, 0, 0);
+  }
+  int e;
+  if (logits) {
+    const uint64_t mine = topk_token<V>(logits + (size_t)t * E, E, k, cand[wave], sel[wave]);
+    e = ~__builtin_amdgcn_readlane((int)(uint32_t)mine, j);  // selection j's expert
+    if (j == 0 && blockIdx.y == 0 && wave == 0) {
+      const float g = topk_gate_of(mine, k);
+      if (lane < k) {
+        idx[(size_t)t * k + lane] = topk_key_index(mine);
+        gate[(size_t)t * k + lane] = g;
+      }
+    }
+  } else {
+    e = idx[pair];
+    if (e < 0 || e >= E) return;  // dropped pair: never read downstream
   }
   // buffers over this row tile's K tiles (codes) and scale groups
   const size_t row = (size_t)e * RT + rt;
@@ -374,20 +397,29 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
 static size_t gateup_lds_bytes(int d) { return (size_t)4 * 1024 * gu_x_copies(d); }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const int32_t* idx, float* h32, hipStream_t st) {
+                              const float* logits, int32_t* idx, float* gate, float* h32,
+                              hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
   const size_t lds = gateup_lds_bytes(s.d);
-#define K3_GATEUP(XC)                                                                          \
-  hipLaunchKernelGGL(gemv_gateup_kernel<XC>, g1, dim3(256), lds, st, x, s.d, s.f, s.k, s.E,    \
-                     w.gate_q, w.gate_s, w.up_q, w.up_s, idx, h32)
+#define K3_GATEUP(XC, V)                                                                       \
+  hipLaunchKernelGGL((gemv_gateup_kernel<XC, V>), g1, dim3(256), lds, st, x, s.d, s.f, s.k,   \
+                     s.E, w.gate_q, w.gate_s, w.up_q, w.up_s, logits, idx, gate, h32)
+#define K3_GATEUP_V(XC)                                                                        \
+  do {                                                                                         \
+    if (s.E <= 1024)                                                                           \
+      K3_GATEUP(XC, 16);                                                                       \
+    else                                                                                       \
+      K3_GATEUP(XC, 64);                                                                       \
+  } while (0)
   switch (gu_x_copies(s.d)) {
-    case 2: K3_GATEUP(2); break;
-    case 4: K3_GATEUP(4); break;
-    case 8: K3_GATEUP(8); break;
-    case 14: K3_GATEUP(14); break;
-    default: K3_GATEUP(16); break;
+    case 2: K3_GATEUP_V(2); break;
+    case 4: K3_GATEUP_V(4); break;
+    case 8: K3_GATEUP_V(8); break;
+    case 14: K3_GATEUP_V(14); break;
+    default: K3_GATEUP_V(16); break;
   }
+#undef K3_GATEUP_V
 #undef K3_GATEUP
   return hipGetLastError();
 }
@@ -407,13 +439,18 @@ static hipError_t set_down_lds_nc() {
 }
 
 hipError_t prepare_gemv(const Shape& s) {
+  const bool v64 = s.E > 1024;
   const void* gu;
   switch (gu_x_copies(s.d)) {
-    case 2: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<2>); break;
-    case 4: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<4>); break;
-    case 8: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<8>); break;
-    case 14: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<14>); break;
-    default: gu = reinterpret_cast<const void*>(gemv_gateup_kernel<16>); break;
+#define K3_GU(XC)                                                                              \
+  gu = v64 ? reinterpret_cast<const void*>(gemv_gateup_kernel<XC, 64>)                         \
+           : reinterpret_cast<const void*>(gemv_gateup_kernel<XC, 16>)
+    case 2: K3_GU(2); break;
+    case 4: K3_GU(4); break;
+    case 8: K3_GU(8); break;
+    case 14: K3_GU(14); break;
+    default: K3_GU(16); break;
+#undef K3_GU
   }
   const hipError_t e = hipFuncSetAttribute(gu, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)gateup_lds_bytes(s.d));

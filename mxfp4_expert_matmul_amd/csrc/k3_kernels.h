@@ -47,8 +47,12 @@ hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* coun
                         int32_t* ntiles, hipStream_t st);
 
 // gemv.hip (decode path, T <= kGemvMaxT)
+// logits != NULL: each pair's expert comes from a top-k selection of its
+// token's logits inside the kernel, which also writes idx and gate; else idx
+// is the routing (gate unused)
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const int32_t* idx, float* h32, hipStream_t st);
+                              const float* logits, int32_t* idx, float* gate, float* h32,
+                              hipStream_t st);
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st);
 // once per handle: raise the dynamic LDS limit the decode down kernel needs

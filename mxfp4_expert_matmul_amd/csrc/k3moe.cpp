@@ -175,25 +175,31 @@ hipError_t stage(k3moe* h, int id, hipStream_t st, F&& launch) {
   return hipSuccess;
 }
 
+// Router logits, then (with_topk) the top-k selection into idx and gate.
 int run_router(k3moe* h, const uint16_t* x, int T, float* logits, int32_t* idx, float* gate,
-               hipStream_t st) {
+               hipStream_t st, bool with_topk = true) {
   const Shape s = shape_of(h);
   hipError_t e = stage(h, K3MOE_STAGE_ROUTER_LOGITS, st, [&] {
     return k3::launch_router_logits(x, T, s, h->w.router_w, h->wr3, h->w.router_b, logits, st);
   });
   if (e != hipSuccess) return K3MOE_EHIP;
+  if (!with_topk) return K3MOE_OK;
   e = stage(h, K3MOE_STAGE_TOPK, st, [&] { return k3::launch_topk(logits, T, s, idx, gate, st); });
   return hip_status(e);
 }
 
-int run_experts(k3moe* h, const uint16_t* x, int T, const int32_t* idx, const float* gate,
-                float* y, hipStream_t st) {
+// The expert FFNs and the combine. With `logits` (GEMV path only) the
+// gate/up GEMV selects each token's experts itself and writes idx and gate;
+// otherwise idx and gate are the routing and are only read.
+int run_experts(k3moe* h, const uint16_t* x, int T, int32_t* idx, float* gate, float* y,
+                hipStream_t st, const float* logits = nullptr) {
   const Shape s = shape_of(h);
   const k3::ExpertWeights w = experts_of(h);
   hipError_t e;
   if (T <= k3::kGemvMaxT) {
-    e = stage(h, K3MOE_STAGE_GATEUP, st,
-              [&] { return k3::launch_gemv_gateup(x, T, s, w, idx, h->h32, st); });
+    e = stage(h, K3MOE_STAGE_GATEUP, st, [&] {
+      return k3::launch_gemv_gateup(x, T, s, w, logits, idx, gate, h->h32, st);
+    });
     if (e != hipSuccess) return K3MOE_EHIP;
     e = stage(h, K3MOE_STAGE_DOWN, st,
               [&] { return k3::launch_gemv_down(T, s, w, idx, gate, h->h32, y, st); });
@@ -383,8 +389,9 @@ int k3moe_experts_forward(k3moe* h, const void* x, int32_t T, const int32_t* idx
     return K3MOE_EINVAL;
   DeviceGuard guard(h->device);
   if (!guard.ok) return K3MOE_EHIP;
-  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y,
-                     static_cast<hipStream_t>(stream));
+  // without logits run_experts only reads idx and gate
+  return run_experts(h, static_cast<const uint16_t*>(x), T, const_cast<int32_t*>(idx),
+                     const_cast<float*>(gate), y, static_cast<hipStream_t>(stream));
 }
 
 int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y, int32_t* topk_idx,
@@ -400,9 +407,13 @@ int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y, int32_t* t
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = topk_idx ? topk_idx : h->idx;
   float* gate = topk_gate ? topk_gate : h->gate;
-  int rc2 = run_router(h, static_cast<const uint16_t*>(x), T, h->logits, idx, gate, st);
+  // few tokens: the gate/up GEMV does the top-k selection (one launch fewer)
+  const bool fused_topk = T <= k3::kGemvMaxT;
+  int rc2 = run_router(h, static_cast<const uint16_t*>(x), T, h->logits, idx, gate, st,
+                       !fused_topk);
   if (rc2 != K3MOE_OK) return rc2;
-  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y, st);
+  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y, st,
+                     fused_topk ? h->logits : nullptr);
 }
 
 
