@@ -12,6 +12,7 @@ from scipy.special import expit, softmax
 
 import oracle
 import synth
+from _dense_check import dense_masked_forward
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -239,9 +240,14 @@ def test_dense_masked_equals_sparse(ci, T):
     src = synth.ExpertSource(cfg, W)
     x = synth.gen_x(cfg, T=T)
     wr = synth.gen_router_w(cfg)
-    sparse = oracle.layer_forward(x, wr, None, src, cfg.k)["y64"]
-    dense = oracle.dense_masked_forward(x, wr, None, src, cfg.k, cfg.E)
+    r = oracle.layer_forward(x, wr, None, src, cfg.k)
+    sparse = r["y64"]
+    dense, mask = dense_masked_forward(x, wr, None, src, cfg.k, cfg.E)
+    for t in range(T):  # the same experts are selected
+        assert set(np.nonzero(mask[t])[0]) == set(r["idx"][t].tolist())
     rms = np.sqrt(np.mean(sparse ** 2))
+    # fp64 with different summation orders (BLAS products vs the oracle's
+    # index-order sums): agreement to a few ulps of the accumulated terms
     assert np.max(np.abs(dense - sparse)) <= 1e-12 * rms
 
 
@@ -273,3 +279,48 @@ def test_group_pairs_matches_stable_sort(T, k, E):
     assert np.array_equal(counts, np.bincount(flat, minlength=E))
     assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
     assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+
+
+def test_failed_expert_contributes_zero():
+    # a slot whose expert index is outside [0, E) adds nothing (the pages'
+    # batched-prefill fix: a failed expert contributes zero, never garbage)
+    cfg = synth.CONFIGS[0]
+    W = synth.gen_weights(cfg)
+    src = synth.ExpertSource(cfg, W)
+    x = synth.gen_x(cfg, T=3)
+    idx = np.array([[1, 4], [2, 7], [0, 5]], dtype=np.int32)
+    gate = np.array([[0.75, 0.25], [0.5, 0.5], [0.9, 0.1]])
+    bad = idx.copy()
+    bad[0, 1], bad[2, 0] = cfg.E, -1
+    y_bad = oracle.experts_forward(x, bad, gate, src, n_experts=cfg.E)
+    g0 = gate.copy()
+    g0[0, 1] = g0[2, 0] = 0.0
+    y_ref = oracle.experts_forward(x, idx, g0, src, n_experts=cfg.E)
+    assert np.array_equal(y_bad, y_ref)
+    single = oracle.expert_ffn(oracle.bf16_to_f64(x[2:3]), src(5))[0]
+    assert np.array_equal(y_bad[2], 0.0 + 0.1 * single)
+
+
+def test_group_pairs_leaves_out_invalid():
+    idx = np.array([[2, 0], [9, 2], [-1, 1]], dtype=np.int32)
+    counts, offsets, perm = oracle.group_pairs(idx, 3)
+    assert counts.tolist() == [1, 1, 2]
+    assert offsets.tolist() == [0, 1, 2, 4]
+    assert perm.tolist() == [1, 5, 0, 3]
+
+
+def test_thread_count_does_not_change_results():
+    cfg = synth.CONFIGS[1]
+    src = synth.ExpertSource(cfg, synth.gen_weights(cfg))
+    x = synth.gen_x(cfg, T=5)
+    wr = synth.gen_router_w(cfg)
+    before = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        a = oracle.layer_forward(x, wr, None, src, cfg.k)
+        oracle.set_threads(4)
+        b = oracle.layer_forward(x, wr, None, src, cfg.k)
+    finally:
+        oracle.set_threads(before)
+    assert np.array_equal(a["logits"], b["logits"])
+    assert np.array_equal(a["y64"], b["y64"])
