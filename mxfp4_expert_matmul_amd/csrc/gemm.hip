@@ -323,9 +323,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 //    p ^ (t % 8), so the 8 lanes of a 128-byte read see distinct bank groups.
 //  - gate/up (FP6 x): rows of 96 bytes, packed (a copy fills 8 rows per
 //    1 KB); the six 16-byte chunks of row t are rotated by rot6(t). A lane
-//    reads its block as a 16-byte and an 8-byte part; with this rotation the
-//    16-byte reads of 8 lanes hit distinct bank groups (at most 2-way for
-//    the 8-byte reads).
+//    reads the chunk holding the 16-byte part of its block and the chunk
+//    holding its 8-byte part (two 16-byte reads); with this rotation both
+//    reads of any 8 (or 16) lanes hit distinct bank groups.
 template <int MODE>
 struct ActLds;
 template <>
@@ -539,12 +539,20 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       int sa6 = (3 * g + 1) / 2 + rot;
       sa6 = sa6 == 6 ? 0 : sa6;
       const int sb6 = 1 + 3 * (g >> 1) + rot;
-      const int oa = kActRow6 * tr + 16 * sa6, ob = kActRow6 * tr + 16 * sb6 + 8 * (g & 1);
+      // the tail chunk is read whole (a 16-byte read, like the head: 8-byte
+      // reads of one half by 16 lanes would meet 2-way bank conflicts) and
+      // the lane keeps its half
+      const int oa = kActRow6 * tr + 16 * sa6, ob = kActRow6 * tr + 16 * sb6;
       const bool tail_first = g & 1;
+      const uint4 th = *reinterpret_cast<const uint4*>(&L.a[0][ob]);
+      const uint4 tl = *reinterpret_cast<const uint4*>(&L.a[1][ob]);
+      // keeps both reads whole (the compiler would otherwise narrow each to the
+      // lane's half, an 8-byte read of one half by 16 lanes: 2-way conflicts)
+      asm volatile("" ::"v"(__builtin_bit_cast(v4i, th)), "v"(__builtin_bit_cast(v4i, tl)));
       b.hi = fp6_operand(*reinterpret_cast<const uint4*>(&L.a[0][oa]),
-                         *reinterpret_cast<const uint2*>(&L.a[0][ob]), tail_first);
+                         tail_first ? make_uint2(th.z, th.w) : make_uint2(th.x, th.y), tail_first);
       b.lo = fp6_operand(*reinterpret_cast<const uint4*>(&L.a[1][oa]),
-                         *reinterpret_cast<const uint2*>(&L.a[1][ob]), tail_first);
+                         tail_first ? make_uint2(tl.z, tl.w) : make_uint2(tl.x, tl.y), tail_first);
     } else {
       const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
       b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
