@@ -7,25 +7,25 @@
 // section), so one tile reads an expert's weight rows once for up to
 // kTileM tokens.
 //
-// Activations (x into gate/up, the SwiGLU output h into down) must reach the
-// MFMA without losing much precision, so each 32-element block is split into
-// two FP6 (E2M3) terms with their own E8M0 scales, v ~= s1*hi + s2*lo:
-// s1 = 2^(floor(log2 max|v|) - 2) puts the block max in [4, 8) (values that
-// round to 8 saturate at 7.5 and the residual keeps the difference), s2 comes
-// from the block max of the residual. FP4 x FP6 MFMAs run at the FP4 rate and
-// a term is 24 bytes per block. Each term is one MFMA, accumulated in fp32.
+// Activations are bf16 and must reach the MFMA without losing precision, so
+// each 32-element block of x is split into two E4M3 terms with their own E8M0
+// scales, x ~= s1*hi + s2*lo, s1 = 2^(floor(log2 max|x|) - 7) (block max in
+// [128, 256): no clamping), s2 from the block max of the residual; the pair
+// reproduces bf16 blocks to within about 2^-16 of the block max. The SwiGLU
+// output h (fp32) is split the same way before the down projection. Each
+// term is one MFMA, accumulated in fp32.
 //
 // Operand lane layouts (measured on gfx950 for 16x16x128 f8f6f4):
 //   lane l: row/column r = l % 16, lane group g = l / 16
 //   FP4 operand: 16 bytes = K slots 32g .. 32g+31 (element 2i low nibble)
-//   FP6 operand: 24 bytes = K slots 32g .. 32g+31, 6 bits each, slot s at
-//                bits 6s .. 6s+5 of the little-endian 192-bit value
+//   FP8 operand: bytes 0-15 = K slots 16g .. 16g+15,
+//                bytes 16-31 = K slots 64+16g .. 64+16g+15
 //   scale operand of lane l: row/column r, K slots 32g .. 32g+31
 //   result: lane l, element i -> row 4g + i of A, column l % 16 of B
 // One MFMA step covers one 128-column K tile: the weight lane (r, g) holds
 // the tile's 32-column block g of row r, and the activation lane (r, g) the
-// same block g of token r, so every K slot pairs the same physical column on
-// both sides.
+// 16-column pieces g and 4 + g of token r, so every K slot pairs the same
+// physical column on both sides.
 #include <type_traits>
 
 #include "k3_device.h"
@@ -33,54 +33,14 @@
 
 namespace k3 {
 
-constexpr int kFmtFp6 = 2;  // E2M3
+constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed (nt)
 
 // ------------------------------------------------------------- split of x
-// E8M0 byte of the scale 2^(floor(log2 amax) - 2) that maps the block max
-// into [4, 8) of E2M3; amax == 0 gives 127.
-__device__ __forceinline__ uint32_t e2m3_block_scale_byte(float amax) {
-  if (!(amax > 0.0f)) return 127u;
-  int b = ilog2_f32(amax) - 2 + 127;
-  if (b < 0) b = 0;
-  if (b > 254) b = 254;
-  return (uint32_t)b;
-}
-
-// Nearest E2M3 value (round to nearest even), saturating at +-7.5. E2M3:
-// sign, 2 exponent bits (bias 1), 3 mantissa bits; spacing 1/8 below 2
-// (subnormals included), 1/4 in [2, 4), 1/2 in [4, 8).
-__device__ __forceinline__ float round_e2m3(float a) {
-  const float m = fabsf(a);
-  if (m == 0.0f) return a;
-  int e = ilog2_f32(m);
-  if (e < 0) e = 0;
-  const float ulp = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
-  const float inv = __uint_as_float((uint32_t)(3 - e + 127) << 23);  // 1 / ulp, exact
-  const float q = rintf(a * inv) * ulp;
-  return fminf(fmaxf(q, -7.5f), 7.5f);
-}
-
-// 6-bit code of a value that E2M3 represents exactly.
-__device__ __forceinline__ uint32_t e2m3_code(float q) {
-  const float m = fabsf(q);
-  const float c = m < 2.0f ? 8.0f * m : (m < 4.0f ? 8.0f + 4.0f * m : 16.0f + 2.0f * m);
-  return (uint32_t)c | ((__float_as_uint(q) >> 31) << 5);
-}
-
-// Puts the 6-bit code of slot j of a 32-value FP6 block into its 24 bytes
-// (slot j at bits 6j .. 6j+5), as the FP6 MFMA operand holds them.
-__device__ __forceinline__ void pack_e2m3_slot(uint32_t (&w)[6], int j, uint32_t c) {
-  const int bp = 6 * j;
-  w[bp >> 5] |= c << (bp & 31);
-  if ((bp & 31) > 26) w[(bp >> 5) + 1] |= c >> (32 - (bp & 31));
-}
-
-// One thread per 32-element block of x: two E2M3 terms, 24 bytes each at
-// 24 * block in their planes, and their scale bytes.
+// One thread per 32-element block of x.
 __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int nblk,
-                                                      uint8_t* __restrict__ xq_hi,
+                                                      int nb, uint8_t* __restrict__ xq_hi,
                                                       uint8_t* __restrict__ xq_lo,
                                                       uint8_t* __restrict__ xs_hi,
                                                       uint8_t* __restrict__ xs_lo) {
@@ -101,43 +61,46 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const uint32_t b1 = e2m3_block_scale_byte(amax);
+  const uint32_t b1 = e4m3_block_scale_byte(amax);
   const float s1 = e8m0_to_f32(b1), s1inv = e8m0_to_f32(254u - b1);
-  // the first term is packed as it is rounded; v keeps the residual
-  uint32_t ph[6] = {0u, 0u, 0u, 0u, 0u, 0u}, pl[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+  float hi[32], r[32];
   float ramax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    const float h = round_e2m3(v[j] * s1inv);
-    pack_e2m3_slot(ph, j, e2m3_code(h));
-    v[j] = v[j] - h * s1;
-    ramax = fmaxf(ramax, fabsf(v[j]));
+    hi[j] = round_e4m3(v[j] * s1inv);
+    r[j] = v[j] - hi[j] * s1;
+    ramax = fmaxf(ramax, fabsf(r[j]));
   }
-  const uint32_t b2 = e2m3_block_scale_byte(ramax);
+  const uint32_t b2 = e4m3_block_scale_byte(ramax);
   const float s2inv = e8m0_to_f32(254u - b2);
+  uint32_t ph[8], pl[8];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) pack_e2m3_slot(pl, j, e2m3_code(round_e2m3(v[j] * s2inv)));
-  uint2* dh = reinterpret_cast<uint2*>(xq_hi + (size_t)i * 24);
-  uint2* dl = reinterpret_cast<uint2*>(xq_lo + (size_t)i * 24);
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    dh[q] = make_uint2(ph[2 * q], ph[2 * q + 1]);
-    dl[q] = make_uint2(pl[2 * q], pl[2 * q + 1]);
+  for (int q = 0; q < 8; ++q) {
+    ph[q] = pack4_e4m3(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+    pl[q] = pack4_e4m3(round_e4m3(r[4 * q] * s2inv), round_e4m3(r[4 * q + 1] * s2inv),
+                       round_e4m3(r[4 * q + 2] * s2inv), round_e4m3(r[4 * q + 3] * s2inv));
   }
+  uint4* dh = reinterpret_cast<uint4*>(xq_hi + (size_t)i * 32);
+  uint4* dl = reinterpret_cast<uint4*>(xq_lo + (size_t)i * 32);
+  dh[0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+  dh[1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
+  dl[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+  dl[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
   xs_hi[i] = (uint8_t)b1;
   xs_lo[i] = (uint8_t)b2;
+  (void)nb;
 }
-
-// Bytes of one FP6 term plane of n rows of d values: 24 per 32-value block.
-static size_t x_plane_bytes(int n, int d) { return (size_t)n * (d / 32) * 24; }
 
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,
                           hipStream_t st) {
   const int nb = d / 32;
   const int nblk = T * nb;
   if (nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + 255) / 256), dim3(256), 0, st, x, nblk, xq,
-                     xq + x_plane_bytes(T, d), xs, xs + (size_t)T * nb);
+  const size_t plane = (size_t)T * d, splane = (size_t)T * nb;
+  (void)plane;
+  (void)splane;
+  hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + 255) / 256), dim3(256), 0, st, x, nblk, nb, xq,
+                     xq + (size_t)T * d, xs, xs + (size_t)T * nb);
   return hipGetLastError();
 }
 
@@ -147,25 +110,15 @@ __device__ __forceinline__ v8i fp4_operand(const v4i q) {
   return a;
 }
 
-// FP6 operand from a block's 24 bytes: `head` = its 16-byte part, `tail` =
-// its 8-byte part, which comes first when `tail_first`
-__device__ __forceinline__ v8i fp6_operand(const uint4 head, const uint2 tail, bool tail_first) {
-  v8i b;
-  b[0] = (int)(tail_first ? tail.x : head.x);
-  b[1] = (int)(tail_first ? tail.y : head.y);
-  b[2] = (int)(tail_first ? head.x : head.z);
-  b[3] = (int)(tail_first ? head.y : head.w);
-  b[4] = (int)(tail_first ? head.z : tail.x);
-  b[5] = (int)(tail_first ? head.w : tail.y);
-  b[6] = 0;
-  b[7] = 0;
+__device__ __forceinline__ v8i fp8_operand(const uint4 lo, const uint4 hi) {
+  v8i b = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   return b;
 }
 
 // sa: the A scale register, OPSEL_A picks its byte; sb: the B scale in byte 0
-template <int OPSEL_A, int FMT_B>
-__device__ __forceinline__ v4f mfma_fp4_b(v8i a, int sa, v8i b, int sb, v4f c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp4, FMT_B, OPSEL_A, sa,
+template <int OPSEL_A>
+__device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp4, kFmtFp8, OPSEL_A, sa,
                                                          0, sb);
 }
 
@@ -183,7 +136,7 @@ __device__ __forceinline__ v4f mfma_fp4_b(v8i a, int sa, v8i b, int sb, v4f c) {
 // No two loads of a workgroup read the same bytes: a request for a line
 // that is still in flight stalls the CU's load path.
 //
-// Two workgroups share a CU (39 KB of LDS and at most 256 registers per
+// Two workgroups share a CU (51 KB of LDS and at most 256 registers per
 // lane each), so one computes while the other waits for memory. K is walked
 // one 128-column tile at a time:
 //  - weights (tiled layout, layout.hip) go straight to registers through a
@@ -191,20 +144,20 @@ __device__ __forceinline__ v4f mfma_fp4_b(v8i a, int sa, v8i b, int sb, v4f c) {
 //    operand is one 1 KB tile, one coalesced 16-byte-per-lane buffer load; a
 //    scale dword per lane covers 4 K tiles and is fetched with the group's
 //    first;
-//  - activations (two FP6 terms + scales) of the tile's tokens are copied
+//  - activations (two E4M3 terms + scales) of the tile's tokens are copied
 //    once per workgroup straight into LDS (buffer loads to LDS, two stages,
-//    one tile ahead; layout at ActLds).
-// Every wave issues the same number of loads after its copies in a step, so
-// a stage is known complete by waiting on the wave's load counter down to
-// the count issued after it (s_waitcnt vmcnt(N)), followed by a plain
-// workgroup barrier; the loads of the next stages stay in flight across it
-// (a __syncthreads would wait for all of them).
+//    one tile ahead; 16-byte piece p of token row t at slot p ^ (t % 8), so
+//    the 16 lanes of an MFMA column group read distinct bank groups).
+// Every wave issues the same number of loads per step, so a stage is known
+// complete by waiting on the wave's load counter down to the count issued
+// after it (s_waitcnt vmcnt(N)), followed by a plain workgroup barrier; the
+// loads of the next stages stay in flight across it (a __syncthreads would
+// wait for all of them).
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
 constexpr int kStages = 2;                 // activation ring depth (LDS buffers)
 constexpr int kWStages = 4;                // weight ring depth (register sets)
-constexpr int kActRow6 = 96;               // LDS bytes per token row and term (one K tile:
-                                           // four 24-byte FP6 blocks)
+constexpr int kActRow = 128;               // LDS bytes per token row and term (one K tile)
 constexpr int kScRow = 4;                  // scale bytes per token row and term (4 blocks)
 constexpr int kThreads = 256;
 
@@ -217,13 +170,15 @@ struct GemmShape {
 };
 
 // Loads (vector-memory instructions) one wave issues in the step that
-// computes tile c, in order: its activation copies of tile c + 1 (4 or 5
-// data copies + 1 scale copy), then kWOps weight tiles of tile
+// computes tile c, in order: kActOps activation copies of tile c + 1
+// (kActGroups row groups + 1 scale copy), then kWOps weight tiles of tile
 // c + kWStages - 1, then, when that tile starts a group of 4, kWOps scale
 // dwords for the group. The order is pinned (compiler barriers around each
 // group).
+constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 terms, 4 waves)
 constexpr int kScRows = 128;  // scale rows per term in LDS: two waves copy 64 each (rows past
                               // the tile's tokens read nothing)
+constexpr int kActOps = kActGroups + 1;
 constexpr int kWOps = 4;  // NM * NRT for both modes
 // Counted at the top of the step that computes tile c (P = c % 8): tile c's
 // copies went out one step earlier, followed only by the weights of tile
@@ -305,21 +260,10 @@ __device__ __forceinline__ bool load_tile(int tile, const int32_t* tiles, const 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Activations of one K tile in LDS: token rows of 96 bytes (four 24-byte FP6
-// blocks), packed (a 1 KB copy fills 8 rows); the six 16-byte chunks of row
-// t are rotated by rot6(t). A lane reads the chunk holding the 16-byte part
-// of its block and the chunk holding its 8-byte part (two 16-byte reads);
-// with this rotation both reads of any 8 (or 16) lanes hit distinct bank
-// groups.
 struct ActLds {
-  uint8_t a[2][kTileM * kActRow6];
-  uint8_t s[2][kScRows][kScRow];  // E8M0 scales, one per 32-column block
+  uint8_t a[2][kTileM][kActRow];  // activation terms of one K tile, swizzled
+  uint8_t s[2][kScRows][kScRow];  // their E8M0 scales, one per 32-column block
 };
-constexpr int kX6Copies = 2 * kTileM * kActRow6 / 1024;  // 1 KB copies per K tile (both terms)
-constexpr int kX6PerWave = (kX6Copies + 3) / 4;
-static_assert(kTileM * kActRow6 % 1024 == 0, "FP6 rows must fill whole 1 KB copies");
-
-__device__ __forceinline__ int rot6(int t) { return ((t >> 2) ^ (t >> 3)) & 1; }
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
@@ -329,8 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     const uint8_t* __restrict__ act_lo, const uint8_t* __restrict__ acts_hi,
     const uint8_t* __restrict__ acts_lo, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, int nrb, uint32_t act_bytes, uint32_t sc_bytes,
-    uint8_t* __restrict__ out_hi,
+    const int32_t* __restrict__ ntiles, int nrb, uint32_t act_bytes, uint8_t* __restrict__ out_hi,
     uint8_t* __restrict__ out_lo, uint8_t* __restrict__ outs_hi, uint8_t* __restrict__ outs_lo,
     float* __restrict__ slots) {
   using G = GemmShape<MODE>;
@@ -338,9 +281,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   constexpr int NCT = kTileM / 16;  // 16-token MFMA column tiles per wave
   // separately named buffers (not an array indexed by a runtime number) so
   // reads of one need not wait for the direct-to-LDS copies filling others
-  using Lds = ActLds;
-  __shared__ __attribute__((aligned(16))) Lds lds0;
-  __shared__ __attribute__((aligned(16))) Lds lds1;
+  __shared__ __attribute__((aligned(16))) ActLds lds0;
+  __shared__ __attribute__((aligned(16))) ActLds lds1;
   __shared__ int tok_lds[kTileM];
 
   int tile, rb;
@@ -409,56 +351,46 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       for (int rt = 0; rt < NRT; ++rt) dst[m][rt] = (int)ws_t[m][((size_t)rt * KG + kg) * 64];
   };
 
-  // ---- activations: the 2 x 9 copies of 1 KB (8 packed rows of 96 bytes
-  // each) go to the waves round-robin (copy j to wave j % 4); lane l of copy
-  // j fills chunk slot (16 l % 96) / 16 of row (1024 (j % 9) + 16 l) / 96
-  // with the logical chunk that the row's rotation puts there. A copy (or
-  // part) past the tile's tokens is given an offset beyond the buffer: it
-  // then reads nothing and writes zeros, so no copy sits behind a per-lane
-  // branch and none repeats another's bytes. Scales: wave w copies rows
-  // 64 (w / 2) .. +63 of term w % 2 (4 bytes per lane).
-  // Buffer resources over the activation planes (MUBUF copies, bounds-checked
-  // against the size; word 3 = 32-bit data format, as untyped buffer loads on
-  // this family require); one resource covers both term planes.
+  // ---- activations: wave w copies term w / 2, token rows 64 (w % 2) .. +63
+  // as 8 row groups of 8 (lane -> row + lane / 8, slot lane % 8 holding piece
+  // slot ^ (row % 8)). A row group past the tile's tokens is given an offset
+  // beyond the buffer: the copy then reads nothing and writes zeros, so no
+  // copy sits behind a branch and none repeats another's bytes. Scales: wave
+  // w copies rows 64 (w / 2) .. +63 of term w % 2 (4 bytes per lane).
+  const int term = wave >> 1;
+  const int rbase = (kTileM / 2) * (wave & 1);
+  // buffer resources over the activation planes (MUBUF copies, bounds-checked
+  // against the plane size; word 3 = 32-bit data format, as untyped buffer
+  // loads on this family require)
   const __amdgpu_buffer_rsrc_t act_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(act_hi), 0, (int)act_bytes, 0x00020000);
+      const_cast<uint8_t*>(term ? act_lo : act_hi), 0, (int)act_bytes, 0x00020000);
   const int sterm = wave & 1;
   const int srow0 = 64 * (wave >> 1);
   const __amdgpu_buffer_rsrc_t sc_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(sterm ? acts_lo : acts_hi), 0, (int)sc_bytes, 0x00020000);
-  uint32_t asrc[kX6PerWave];
-  {
-    const uint32_t lo_off = (uint32_t)(act_lo - act_hi);
-    const uint32_t xrow = (uint32_t)nb * 24u;  // bytes of one token row of a term plane
+      const_cast<uint8_t*>(sterm ? acts_lo : acts_hi), 0, (int)(act_bytes >> 5), 0x00020000);
+  uint32_t asrc[kActGroups];
 #pragma unroll
-    for (int i = 0; i < kX6PerWave; ++i) {
-      const int j = wave + 4 * i;
-      const int pos = 1024 * (j % 9) + 16 * lane;
-      const int row = pos / kActRow6, sl = (pos % kActRow6) >> 4;
-      const int c = (sl + 6 - rot6(row)) % 6;
-      asrc[i] = (j < kX6Copies && row < ti.cnt)
-                    ? (j >= 9 ? lo_off : 0u) + (uint32_t)tok_lds[row] * xrow + 16u * (uint32_t)c
-                    : kNoRead;
-    }
+  for (int i = 0; i < kActGroups; ++i) {
+    const int row = rbase + 8 * i + (lane >> 3);
+    asrc[i] = (rbase + 8 * i < ti.cnt)
+                  ? (uint32_t)tok_lds[row] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (row & 7))
+                  : kNoRead;
   }
   const int srow = srow0 + lane;
   const uint32_t sc_off = srow < ti.cnt ? (uint32_t)tok_lds[srow] * (uint32_t)nb : kNoRead;
-  auto act_issue = [&](Lds& L, int kt) {
-    const int kb = kt * kActRow6;
+  auto act_issue = [&](ActLds& L, int kt) {
+    const int kb = kt * 128;
 #pragma unroll
-    for (int i = 0; i < kX6PerWave; ++i) {
-      const int j = wave + 4 * i;  // wave-uniform
-      if (j < kX6Copies)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            act_rs, (lds_ptr)&L.a[j >= 9 ? 1 : 0][1024 * (j % 9)], 16, (int)asrc[i], kb, 0, 0);
-    }
+    for (int i = 0; i < kActGroups; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_ptr)&L.a[term][rbase + 8 * i][0], 16,
+                                               (int)asrc[i], kb, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_rs, (lds_ptr)&L.s[sterm][srow0][0], 4, (int)sc_off,
                                              4 * kt, 0, 0);
   };
   // one step's loads: the copy of tile ka (clamped to the last tile so the
   // tail issues the same loads; that stage is never read), then the weights
   // of tile kw (nothing past the last tile)
-  auto stage_issue = [&](Lds& L, int ka, WStage& ws, int kw) {
+  auto stage_issue = [&](ActLds& L, int ka, WStage& ws, int kw) {
     ka = min(ka, KT - 1);
     issue_fence();
     act_issue(L, ka);
@@ -475,37 +407,26 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // B operands of one 16-token column tile, both terms, and the terms'
-  // scales of 32-column block g: block g of the token row (K slots 32g..),
-  // 24 bytes = chunk (3g + 1) / 2 whole and the low (g even) or high (g odd)
-  // half of chunk 1 + 3 (g / 2), before the row's rotation.
+  // B operands of one 16-token column tile: pieces g and 4 + g of the token
+  // row (K slots 16g.. and 64 + 16g.. of the MFMA), both terms, and the
+  // terms' scales of 32-column block g
   struct BFrag {
     v8i hi, lo;
     int shi, slo;
   };
-  auto b_load = [&](const Lds& L, int ct, BFrag& b) {
+  auto b_load = [&](const ActLds& L, int ct, BFrag& b) {
     const int tr = m0 + 16 * ct + r;
-    const int rot = rot6(tr);
-    int sa6 = (3 * g + 1) / 2 + rot;
-    sa6 = sa6 == 6 ? 0 : sa6;
-    const int sb6 = 1 + 3 * (g >> 1) + rot;
-    const int oa = kActRow6 * tr + 16 * sa6, ob = kActRow6 * tr + 16 * sb6;
-    const bool tail_first = g & 1;
-    const uint4 th = *reinterpret_cast<const uint4*>(&L.a[0][ob]);
-    const uint4 tl = *reinterpret_cast<const uint4*>(&L.a[1][ob]);
-    // keeps the tail reads whole 16-byte reads: narrowed to the lane's half,
-    // 16 lanes reading one half each meet 2-way bank conflicts
-    asm volatile("" ::"v"(__builtin_bit_cast(v4i, th)), "v"(__builtin_bit_cast(v4i, tl)));
-    b.hi = fp6_operand(*reinterpret_cast<const uint4*>(&L.a[0][oa]),
-                       tail_first ? make_uint2(th.z, th.w) : make_uint2(th.x, th.y), tail_first);
-    b.lo = fp6_operand(*reinterpret_cast<const uint4*>(&L.a[1][oa]),
-                       tail_first ? make_uint2(tl.z, tl.w) : make_uint2(tl.x, tl.y), tail_first);
+    const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
+    b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
+                       *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
+    b.lo = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
+                       *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
     b.shi = L.s[0][tr][g];
     b.slo = L.s[1][tr][g];
   };
   // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
   // next column tile's B operands are read while this one's MFMAs run.
-  auto compute = [&](const Lds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc) {
+  auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc) {
     constexpr int P = decltype(pc)::value;
     BFrag b[2];
     b_load(L, 0, b[0]);
@@ -519,13 +440,13 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt)
             acc[m][rt][ct] =
-                mfma_fp4_b<P, kFmtFp6>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.hi, cb.shi, acc[m][rt][ct]);
+                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.hi, cb.shi, acc[m][rt][ct]);
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt)
             acc[m][rt][ct] =
-                mfma_fp4_b<P, kFmtFp6>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.lo, cb.slo, acc[m][rt][ct]);
+                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.lo, cb.slo, acc[m][rt][ct]);
       }
     }
   };
@@ -536,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // tile c's copies (its weights, issued earlier, have landed too), barrier,
   // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
   // group's scale dwords when c + 3 starts one), compute tile c.
-  auto step = [&](auto pc, const Lds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
-                  Lds& Ln, WStage& Wn, int c) {
+  auto step = [&](auto pc, const ActLds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
+                  ActLds& Ln, WStage& Wn, int c) {
     constexpr int P = decltype(pc)::value;
     wait_vmcnt<loads_after_act<P>()>();
     stage_barrier();
@@ -589,12 +510,9 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   if (!wave_on) return;
 
   if (MODE == kGateUp) {
-    // h = SiLU(g) * u, split into two FP6 terms per 32 features. The wave's
+    // h = SiLU(g) * u, split into two E4M3 terms per 32 features (the wave's
     // 32 features are one MX block; lane (r, g) holds features 16 rt + 4 g + i
-    // of token column r, which are FP6 slots at bytes 3 g .. 3 g + 2 (rt = 0)
-    // and 12 + 3 g .. (rt = 1) of the block's 24 bytes. Lane groups 0..2
-    // write dwords g and 3 + g of each term's block from their own 3 bytes and
-    // those of the next lane group.
+    // of token column r).
     const int nbf = f_out >> 5;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -610,43 +528,33 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
         }
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      const uint32_t b1 = e2m3_block_scale_byte(amax);
+      const uint32_t b1 = e4m3_block_scale_byte(amax);
       const float s1 = e8m0_to_f32(b1), s1inv = e8m0_to_f32(254u - b1);
-      uint32_t pk[2][2] = {{0u, 0u}, {0u, 0u}};  // [term][rt]: 4 codes in 24 bits
+      float hi[2][4], rs[2][4];
       float ramax = 0.0f;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float q = round_e2m3(h[rt][i] * s1inv);
-          pk[0][rt] |= e2m3_code(q) << (6 * i);
-          h[rt][i] = h[rt][i] - q * s1;
-          ramax = fmaxf(ramax, fabsf(h[rt][i]));
+          hi[rt][i] = round_e4m3(h[rt][i] * s1inv);
+          rs[rt][i] = h[rt][i] - hi[rt][i] * s1;
+          ramax = fmaxf(ramax, fabsf(rs[rt][i]));
         }
       ramax = fmaxf(ramax, __shfl_xor(ramax, 16, 64));
       ramax = fmaxf(ramax, __shfl_xor(ramax, 32, 64));
-      const uint32_t b2 = e2m3_block_scale_byte(ramax);
+      const uint32_t b2 = e4m3_block_scale_byte(ramax);
       const float s2inv = e8m0_to_f32(254u - b2);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[1][rt] |= e2m3_code(round_e2m3(h[rt][i] * s2inv)) << (6 * i);
-      uint32_t nx[2][2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) nx[q][rt] = (uint32_t)__shfl_down((int)pk[q][rt], 16, 64);
       const int i = m0 + 16 * ct + r;
       if (i < ti.cnt) {
         const size_t pos = (size_t)ti.base + ti.row0 + i;
-        const size_t blk = (pos * nbf + (w0 >> 5)) * 24;
-        if (g < 3) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-              *reinterpret_cast<uint32_t*>((q ? out_lo : out_hi) + blk + 12 * rt + 4 * g) =
-                  (pk[q][rt] >> (8 * g)) | (nx[q][rt] << (24 - 8 * g));
+        for (int rt = 0; rt < 2; ++rt) {
+          const size_t off = pos * f_out + w0 + 16 * rt + 4 * g;
+          *reinterpret_cast<uint32_t*>(out_hi + off) =
+              pack4_e4m3(hi[rt][0], hi[rt][1], hi[rt][2], hi[rt][3]);
+          *reinterpret_cast<uint32_t*>(out_lo + off) =
+              pack4_e4m3(round_e4m3(rs[rt][0] * s2inv), round_e4m3(rs[rt][1] * s2inv),
+                         round_e4m3(rs[rt][2] * s2inv), round_e4m3(rs[rt][3] * s2inv));
         }
         if (g == 0) {
           outs_hi[pos * nbf + (w0 >> 5)] = (uint8_t)b1;
@@ -715,13 +623,12 @@ hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, con
                               uint8_t* hq, uint8_t* hs, hipStream_t st) {
   if (T <= 0 || max_tiles <= 0) return hipSuccess;
   const size_t P = (size_t)T * s.k;
-  const size_t xplane = x_plane_bytes(T, s.d), xsplane = (size_t)T * (s.d / 32);
-  const size_t hplane = x_plane_bytes((int)P, s.f), hsplane = P * (s.f / 32);
+  const size_t xplane = (size_t)T * s.d, xsplane = (size_t)T * (s.d / 32);
+  const size_t hplane = P * s.f, hsplane = P * (s.f / 32);
   const int nrb = s.f / GemmShape<kGateUp>::kRowsPerBlock;
   hipLaunchKernelGGL(mx_gemm_kernel<kGateUp>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
                      st, s.d, s.f, s.f, s.k, w.gate_q, w.gate_s, w.up_q, w.up_s, xq, xq + xplane,
-                     xs, xs + xsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)(2 * xplane),
-                     (uint32_t)xsplane, hq, hq + hplane, hs,
+                     xs, xs + xsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)xplane, hq, hq + hplane, hs,
                      hs + hsplane, nullptr);
   return hipGetLastError();
 }
@@ -732,13 +639,12 @@ hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const
                             hipStream_t st) {
   if (T <= 0 || max_tiles <= 0) return hipSuccess;
   const size_t P = (size_t)T * s.k;
-  const size_t hplane = x_plane_bytes((int)P, s.f), hsplane = P * (s.f / 32);
+  const size_t hplane = P * s.f, hsplane = P * (s.f / 32);
   constexpr int rpb = GemmShape<kDown>::kRowsPerBlock;
   const int nrb = (s.d + rpb - 1) / rpb;
   hipLaunchKernelGGL(mx_gemm_kernel<kDown>, dim3(gemm_grid(max_tiles, nrb)), dim3(kThreads), 0,
                      st, s.f, s.d, s.f, s.k, w.down_q, w.down_s, nullptr, nullptr, hq, hq + hplane,
-                     hs, hs + hsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)(2 * hplane),
-                     (uint32_t)hsplane, nullptr, nullptr, nullptr,
+                     hs, hs + hsplane, offsets, perm, tiles, ntiles, nrb, (uint32_t)hplane, nullptr, nullptr, nullptr,
                      nullptr, slots);
   return hipGetLastError();
 }

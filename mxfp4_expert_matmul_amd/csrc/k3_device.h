@@ -10,6 +10,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -78,6 +79,36 @@ __device__ __forceinline__ int ilog2_f32(float a) {
   int e = (int)(u >> 23);
   if (e != 0) return e - 127;
   return -127 - (__clz(u) - 9);  // subnormal: leading mantissa bit position
+}
+
+// Round an fp32 value to the nearest OCP E4M3 value (ties to even), for
+// |a| < 464 (no saturation needed). Returns the rounded value as fp32.
+__device__ __forceinline__ float round_e4m3(float a) {
+  float m = fabsf(a);
+  if (m == 0.0f) return a;
+  int e = ilog2_f32(m);
+  if (e < -6) e = -6;  // subnormal spacing 2^-9
+  float ulp = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
+  return rintf(a / ulp) * ulp;
+}
+
+// E8M0 byte of the scale 2^(floor(log2 amax) - 7) that maps the block max
+// into [128, 256) of E4M3 (no clamping at 448); amax == 0 gives 127.
+__device__ __forceinline__ uint32_t e4m3_block_scale_byte(float amax) {
+  if (!(amax > 0.0f)) return 127u;
+  int b = ilog2_f32(amax) - 7 + 127;
+  if (b < 0) b = 0;
+  if (b > 254) b = 254;
+  return (uint32_t)b;
+}
+
+// Pack 4 fp32 values that are exactly representable in E4M3 into 4 bytes
+// (hardware convert, round-to-nearest-even, scale 1).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  v2s w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 }  // namespace k3

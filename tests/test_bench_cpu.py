@@ -36,8 +36,8 @@ def test_prefill_bytes_and_flops():
     cfg = synth.CONFIGS[4]
     T, P = cfg.T, cfg.T * cfg.k
     w = 896 * 2 * 7_798_784
-    split_x = 2 * T * cfg.d * 3 // 4 + 2 * T * (cfg.d // 32)  # two FP6 terms + their scales
-    split_h = 2 * P * cfg.f * 3 // 4 + 2 * P * (cfg.f // 32)  # two FP6 terms + their scales
+    split_x = 2 * T * cfg.d + 2 * T * (cfg.d // 32)  # two E4M3 terms + their scales
+    split_h = 2 * P * cfg.f + 2 * P * (cfg.f // 32)  # two E4M3 terms + their scales
     assert bench.algorithmic_bytes(cfg, T, 896, "gateup") == w + split_x + split_h
     assert bench.algorithmic_bytes(cfg, T, 896, "combine") == P * cfg.d * 4 + P * 8 + T * cfg.d * 4
     # router at T=4096: 2*T*E*d flops; experts: 3 matrices of 2*d*f per pair

@@ -166,6 +166,59 @@ def test_skewed_bias_small(k3):
     layer.close()
 
 
+class Custom(Small):
+    """A small layer with caller-chosen weights (host and device)."""
+
+    def __init__(self, cfg, W):
+        import mxfp4_expert_matmul_amd as k3m
+        from synth.device import host_weights_to_device
+        self.cfg = cfg
+        self.W = W
+        self.wr = synth.gen_router_w(cfg)
+        self.bias = None
+        self.src = synth.ExpertSource(cfg, W)
+        self.dw = k3m.pack_layer_weights(host_weights_to_device(W, self.wr, None), cfg.E, cfg.d, cfg.f)
+
+
+EDGE = synth.LayerConfig("edge_d256_e8_k2_f256", 256, 8, 2, 256, 1, 21)
+
+
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_wide_scale_exponents(k3, T):
+    """E8M0 scale bytes spread over 100..150 (2^-27 .. 2^23), far outside the
+    workload's 123..127: the kernels' scale decoding and the MFMA scale
+    operands must apply each block's own power of two (GEMV path for T <= 4,
+    grouped GEMM above)."""
+    cfg = EDGE
+    W = synth.gen_weights(cfg)
+    rng = np.random.default_rng(31)
+    for name in ("gate_s", "up_s", "down_s"):
+        W[name] = rng.integers(100, 151, W[name].shape).astype(np.uint8)
+    s = Custom(cfg, W)
+    layer = _layer(k3, cfg, s.dw, 64)
+    x = synth.gen_x(cfg, T=T)
+    y, _, _ = _run_and_check(k3, layer, cfg, x, s.src, s.wr, None, label=f"wide scales T={T}")
+    assert np.all(np.isfinite(y))
+    layer.close()
+
+
+@pytest.mark.parametrize("code_byte", [0x00, 0x88])
+def test_zero_codes_give_zero(k3, code_byte):
+    """All codes +0 (0x00) or -0 (0x88): every output is exactly zero on both
+    paths, whatever the scales."""
+    cfg = EDGE
+    W = synth.gen_weights(cfg)
+    for name in ("gate_q", "up_q", "down_q"):
+        W[name] = np.full_like(W[name], code_byte)
+    s = Custom(cfg, W)
+    layer = _layer(k3, cfg, s.dw, 64)
+    for T in (1, 3, 40):
+        y, idx, _ = layer.forward(_x_dev(synth.gen_x(cfg, T=T)))
+        torch.cuda.synchronize()
+        assert np.all(y.cpu().numpy() == 0.0), f"T={T}: non-zero output from zero weights"
+    layer.close()
+
+
 def test_batch_invariance(k3):
     """A token's output does not depend on the batch it is in (chunk-union
     prefill equals the per-token path). Within the grouped-GEMM path only the
