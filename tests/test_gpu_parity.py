@@ -202,6 +202,23 @@ def test_wide_scale_exponents(k3, T):
     layer.close()
 
 
+@pytest.mark.parametrize("T", [3, 64])
+def test_activation_outlier_channels(k3, T):
+    """Four hidden channels 32x larger than the rest (as real activations
+    have): the two-term split keeps each element's own exponent, so the
+    other values of an outlier's block keep their precision (GEMV path for
+    T <= 4, grouped GEMM above)."""
+    cfg = synth.CONFIGS[1]
+    s = Small(cfg, T)
+    layer = _layer(k3, cfg, s.dw, max(T, 8))
+    xf = synth.bf16_bits_to_f32(synth.gen_x(cfg, T=T))
+    ch = np.random.default_rng(41).choice(cfg.d, 4, replace=False)
+    xf[:, ch] *= 32.0  # exact in bf16
+    x = synth.f32_to_bf16_bits(xf)
+    _run_and_check(k3, layer, cfg, x, s.src, s.wr, s.bias, label=f"outlier channels T={T}")
+    layer.close()
+
+
 @pytest.mark.parametrize("code_byte", [0x00, 0x88])
 def test_zero_codes_give_zero(k3, code_byte):
     """All codes +0 (0x00) or -0 (0x88): every output is exactly zero on both
