@@ -4,8 +4,9 @@
 // The (token, slot) pairs p = t*k + j are bucketed by expert with a stable
 // counting sort done in four passes:
 //   1. per-block expert histogram (blocks of kGroupChunk pairs),
-//   2. per-expert column prefix over the blocks (many workgroups): each
-//      block's base within each expert, and the expert counts,
+//   2. per-expert column prefix over the blocks (16 experts x 16 block
+//      segments per workgroup): each block's base within each expert, and
+//      the expert counts,
 //   3. one workgroup: the exclusive prefix sum over experts and the prefill
 //      tile list (expert, first row),
 //   4. per block, each pair's rank among the block's earlier pairs of the
@@ -34,16 +35,16 @@ __global__ __launch_bounds__(256) void group_hist_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < E; e += 256) out[e] = h[e];
 }
 
-// Column prefix over blocks for 64 experts per workgroup: thread (c, q)
-// handles column e0 + c over the blocks of quarter q. bhist[b][e] becomes
-// the count of expert e in blocks before b; counts[e] its total.
-// grid: ceil(E / 64), block 256.
+// Column prefix over blocks for 16 experts per workgroup: thread (c, q)
+// handles column e0 + c over segment q of the blocks (16 segments).
+// bhist[b][e] becomes the count of expert e in blocks before b; counts[e] its
+// total. grid: ceil(E / 16), block 256.
 __global__ __launch_bounds__(256) void group_colscan_kernel(int32_t* __restrict__ bhist, int NB,
                                                             int E, int32_t* __restrict__ counts) {
-  __shared__ int32_t part[4][64];
-  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + c;
-  const int per = (NB + 3) / 4;
+  __shared__ int32_t part[16][16];
+  const int c = threadIdx.x & 15, q = threadIdx.x >> 4;
+  const int e = blockIdx.x * 16 + c;
+  const int per = (NB + 15) / 16;
   const int b0 = q * per, b1 = min(NB, b0 + per);
   int sum = 0;
   if (e < E)
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void group_colscan_kernel(int32_t* __restrict_
       bhist[(size_t)b * E + e] = run;
       run += v;
     }
-    if (q == 3) counts[e] = run;
+    if (q == 15) counts[e] = run;
   }
 }
 
@@ -142,7 +143,7 @@ hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* coun
   if (NB > 0)
     hipLaunchKernelGGL(group_hist_kernel, dim3(NB), dim3(256), 0, st, idx, P, s.E, bhist);
   // with no pairs the column pass writes zero counts (the scan zero offsets)
-  hipLaunchKernelGGL(group_colscan_kernel, dim3((s.E + 63) / 64), dim3(256), 0, st, bhist, NB, s.E,
+  hipLaunchKernelGGL(group_colscan_kernel, dim3((s.E + 15) / 16), dim3(256), 0, st, bhist, NB, s.E,
                      counts);
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, st, counts, s.E, kTileM, offsets,
                      tiles, ntiles);
