@@ -38,68 +38,65 @@ constexpr int kFmtFp4 = 4;
 constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed (nt)
 
 // ------------------------------------------------------------- split of x
-// One thread per 32-element block of x.
-__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int nblk,
-                                                      int nb, uint8_t* __restrict__ xq_hi,
+// Four threads per 32-element block of x, eight elements each: one 16-byte
+// load, the block max over the four lanes by two shuffles, one 8-byte store
+// per term, and the scale bytes from the block's first lane.
+__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int nq,
+                                                      uint8_t* __restrict__ xq_hi,
                                                       uint8_t* __restrict__ xq_lo,
                                                       uint8_t* __restrict__ xs_hi,
                                                       uint8_t* __restrict__ xs_lo) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= nblk) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)i * 32);
-  float v[32];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint4 w = src[q];
+  const int i = blockIdx.x * 256 + threadIdx.x;  // eighth-block index
+  const bool on = i < nq;                         // every lane takes part in the shuffles
+  float v[8];
+  {
+    const uint4 w = on ? reinterpret_cast<const uint4*>(x)[i] : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[8 * q + 2 * j] = bf16_bits_to_f32(ww[j] & 0xffffu);
-      v[8 * q + 2 * j + 1] = bf16_bits_to_f32(ww[j] >> 16);
+      v[2 * j] = bf16_bits_to_f32(ww[j] & 0xffffu);
+      v[2 * j + 1] = bf16_bits_to_f32(ww[j] >> 16);
     }
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const uint32_t b1 = e4m3_block_scale_byte(amax);
   const float s1 = e8m0_to_f32(b1), s1inv = e8m0_to_f32(254u - b1);
-  float hi[32], r[32];
+  float hi[8], r[8];
   float ramax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < 8; ++j) {
     hi[j] = round_e4m3(v[j] * s1inv);
     r[j] = v[j] - hi[j] * s1;
     ramax = fmaxf(ramax, fabsf(r[j]));
   }
+  ramax = fmaxf(ramax, __shfl_xor(ramax, 1, 64));
+  ramax = fmaxf(ramax, __shfl_xor(ramax, 2, 64));
   const uint32_t b2 = e4m3_block_scale_byte(ramax);
   const float s2inv = e8m0_to_f32(254u - b2);
-  uint32_t ph[8], pl[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    ph[q] = pack4_e4m3(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
-    pl[q] = pack4_e4m3(round_e4m3(r[4 * q] * s2inv), round_e4m3(r[4 * q + 1] * s2inv),
-                       round_e4m3(r[4 * q + 2] * s2inv), round_e4m3(r[4 * q + 3] * s2inv));
+  if (!on) return;
+  reinterpret_cast<uint2*>(xq_hi)[i] =
+      make_uint2(pack4_e4m3(hi[0], hi[1], hi[2], hi[3]), pack4_e4m3(hi[4], hi[5], hi[6], hi[7]));
+  reinterpret_cast<uint2*>(xq_lo)[i] =
+      make_uint2(pack4_e4m3(round_e4m3(r[0] * s2inv), round_e4m3(r[1] * s2inv),
+                            round_e4m3(r[2] * s2inv), round_e4m3(r[3] * s2inv)),
+                 pack4_e4m3(round_e4m3(r[4] * s2inv), round_e4m3(r[5] * s2inv),
+                            round_e4m3(r[6] * s2inv), round_e4m3(r[7] * s2inv)));
+  if ((i & 3) == 0) {
+    xs_hi[i >> 2] = (uint8_t)b1;
+    xs_lo[i >> 2] = (uint8_t)b2;
   }
-  uint4* dh = reinterpret_cast<uint4*>(xq_hi + (size_t)i * 32);
-  uint4* dl = reinterpret_cast<uint4*>(xq_lo + (size_t)i * 32);
-  dh[0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-  dh[1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
-  dl[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-  dl[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
-  xs_hi[i] = (uint8_t)b1;
-  xs_lo[i] = (uint8_t)b2;
-  (void)nb;
 }
 
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,
                           hipStream_t st) {
   const int nb = d / 32;
-  const int nblk = T * nb;
-  if (nblk <= 0) return hipSuccess;
-  const size_t plane = (size_t)T * d, splane = (size_t)T * nb;
-  (void)plane;
-  (void)splane;
-  hipLaunchKernelGGL(quant_x_kernel, dim3((nblk + 255) / 256), dim3(256), 0, st, x, nblk, nb, xq,
+  const int nq = T * d / 8;  // eighth-blocks (d % 32 == 0: a block never spans threads of two waves)
+  if (nq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_x_kernel, dim3((nq + 255) / 256), dim3(256), 0, st, x, nq, xq,
                      xq + (size_t)T * d, xs, xs + (size_t)T * nb);
   return hipGetLastError();
 }
