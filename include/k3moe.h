@@ -179,6 +179,69 @@ int k3moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int32_t n, int
 /* Bytes of tiled scales for n matrices of R x K (0 if the shape is invalid). */
 int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K);
 
+/* ---------------------------------------------------------------- expert cache
+ * For models whose experts do not all fit in HBM. The pages' engine streams
+ * the experts of its 2.78T-parameter model from NVMe through an LRU expert
+ * cache in RAM, and counts as "true resident" only the hits on experts that
+ * stayed in the cache from the previous step; raw hits also count experts
+ * its prefetcher has just read in (ssnai.com decision guide; pomoai.com
+ * architecture overview; xugj520.cn run notes, cache statistics;
+ * chenxutan.com, the third reduction). Here the layer's expert weights stay
+ * on the HOST and an HBM arena holds n_slots of them, replaced
+ * least-recently-used. Each forward routes on the GPU, reads
+ * the selection back to the host, copies the experts it misses into free or
+ * least-recently-used slots (over PCIe, on the call's stream), and runs the
+ * expert kernels on the arena with the selection renamed to slots. Results
+ * equal k3moe_layer_forward on the same weights bit for bit (the same
+ * kernels on the same data; only the place of the weights differs).
+ * There is no prefetch: every hit is on an expert resident before the call,
+ * so the raw and the true resident hit rates coincide. */
+typedef struct k3moe_cache k3moe_cache;
+
+/* Host-resident expert weights of a cached layer (HOST struct).
+ *   router_w, router_b: DEVICE pointers as in k3moe_weights, router_b may be
+ *     NULL; BORROWED until k3moe_cache_destroy.
+ *   gate_q .. down_s: HOST pointers to the tiled layout of k3moe_weights
+ *     ([E] experts, each contiguous), BORROWED until k3moe_cache_destroy and
+ *     never written. Page-locked (pinned) memory lets the copies run at full
+ *     PCIe rate; pageable memory works, slower. */
+typedef struct {
+  const float* router_w;
+  const float* router_b;
+  const uint8_t* gate_q;
+  const uint8_t* gate_s;
+  const uint8_t* up_q;
+  const uint8_t* up_s;
+  const uint8_t* down_q;
+  const uint8_t* down_s;
+} k3moe_host_weights;
+
+/* Create a cached layer: cfg as for k3moe_create; n_slots experts in the HBM
+ * arena, cfg->top_k <= n_slots <= cfg->n_experts. A call may route to at most
+ * n_slots distinct experts (else K3MOE_EUNSUPPORTED, nothing run). Allocates
+ * the arena (n_slots x the bytes of one expert) and two handles' workspaces;
+ * K3MOE_ENOMEM if they do not fit. */
+int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int32_t n_slots,
+                       int device, k3moe_cache** out);
+
+/* Forward of the cached layer; arguments as k3moe_layer_forward. The call
+ * waits on the host for the routing (one device-to-host copy of T*k indices)
+ * before it enqueues the expert copies and kernels, so it returns once those
+ * are enqueued, not when they finish. Calls on one cache must use one stream
+ * (or be ordered by the caller). After a failed call the cache forgets every
+ * resident expert (the next call copies what it needs again). */
+int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int32_t* topk_idx,
+                        float* topk_gate, void* stream);
+
+/* Counters since create (HOST outputs, any may be NULL): calls, distinct
+ * experts found resident (hits) and copied in (misses), and bytes copied. */
+int k3moe_cache_stats(const k3moe_cache* c, int64_t* calls, int64_t* hits, int64_t* misses,
+                      int64_t* bytes_in);
+
+/* Destroy: synchronises the device, frees the arena and both handles.
+ * NULL-safe; never frees the weights. */
+void k3moe_cache_destroy(k3moe_cache* c);
+
 /* Stage timing, a profiling aid. Between k3moe_profile_begin and
  * k3moe_profile_end every forward records a HIP event before and after each
  * stage's kernel launch(es) on the call's own stream, for at most max_calls

@@ -93,6 +93,15 @@ def load_library():
     lib.k3moe_profile_begin.restype = ctypes.c_int
     lib.k3moe_profile_end.argtypes = [vp, vp, vp]
     lib.k3moe_profile_end.restype = ctypes.c_int
+    lib.k3moe_cache_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32,
+                                       ctypes.c_int, ctypes.POINTER(vp)]
+    lib.k3moe_cache_create.restype = ctypes.c_int
+    lib.k3moe_cache_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_cache_forward.restype = ctypes.c_int
+    lib.k3moe_cache_stats.argtypes = [vp, vp, vp, vp, vp]
+    lib.k3moe_cache_stats.restype = ctypes.c_int
+    lib.k3moe_cache_destroy.argtypes = [vp]
+    lib.k3moe_cache_destroy.restype = None
     _lib = lib
     return lib
 
@@ -216,6 +225,55 @@ class Layer:
     def close(self):
         if self.handle:
             k3moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CachedLayer:
+    """A layer whose expert weights stay in host memory behind an HBM cache
+    of n_slots experts (k3moe_cache_*). host_weights: router_w / router_b as
+    device tensors, the six expert tensors as host (CPU, ideally pinned)
+    tensors in the tiled layout. All are borrowed: keep them alive."""
+
+    def __init__(self, cfg: Config, host_weights: dict, n_slots: int, device: int = 0):
+        lib = load_library()
+        self.cfg = cfg
+        self._weights = host_weights
+        c = cfg._c()
+        w = _Weights(*[host_weights.get(n).data_ptr() if host_weights.get(n) is not None else None
+                       for n, _ in _Weights._fields_])
+        out = ctypes.c_void_p()
+        _check(lib.k3moe_cache_create(ctypes.byref(c), ctypes.byref(w), int(n_slots), int(device),
+                                      ctypes.byref(out)), "k3moe_cache_create")
+        self.handle = out
+
+    def forward(self, x, stream=None):
+        """Like Layer.forward: returns (y, idx, gate) for x [T][d] bf16 on the GPU."""
+        import torch
+        T = x.shape[0]
+        dev = x.device
+        y = torch.empty((T, self.cfg.d_model), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, self.cfg.top_k), dtype=torch.int32, device=dev)
+        gate = torch.empty((T, self.cfg.top_k), dtype=torch.float32, device=dev)
+        _check(load_library().k3moe_cache_forward(self.handle, _ptr(x), T, _ptr(y), _ptr(idx),
+                                                  _ptr(gate), _stream(stream, dev)),
+               "k3moe_cache_forward")
+        return y, idx, gate
+
+    def stats(self) -> dict:
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(load_library().k3moe_cache_stats(self.handle, *[ctypes.byref(a) for a in v]),
+               "k3moe_cache_stats")
+        return dict(zip(("calls", "hits", "misses", "bytes_in"), (a.value for a in v)))
+
+    def close(self):
+        if self.handle:
+            load_library().k3moe_cache_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -1,0 +1,301 @@
+// Expert cache for layers whose experts live in host memory: an HBM arena of
+// n_slots experts, replaced least-recently-used, filled over PCIe as the
+// routing asks for experts (the GPU counterpart of the pages' LRU expert
+// cache in RAM in front of NVMe; ssnai.com decision guide and xugj520.cn run
+// notes on raw versus true resident hits).
+//
+// A forward: route on the GPU over all E experts (handle `route`), read the
+// selection back, copy in the experts that are not resident, rename the
+// selection to arena slots and run the expert kernels over the arena (handle
+// `arena`, whose "experts" are the slots). The kernels and their data are the
+// ones k3moe_layer_forward uses, so the results are the same bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "k3moe.h"
+
+namespace {
+
+constexpr int kTensors = 6;  // gate codes, gate scales, up codes, up scales, down codes, down scales
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bytes of one expert's share of each tiled tensor.
+void expert_bytes(const k3moe_config* c, size_t (&b)[kTensors]) {
+  const int32_t d = c->d_model, f = c->d_ff;
+  b[0] = (size_t)f * d / 2;
+  b[1] = (size_t)k3moe_tiled_scale_bytes(1, f, d);
+  b[2] = b[0];
+  b[3] = b[1];
+  b[4] = (size_t)d * f / 2;
+  b[5] = (size_t)k3moe_tiled_scale_bytes(1, d, f);
+}
+
+}  // namespace
+
+struct k3moe_cache {
+  k3moe_config cfg;
+  int device;
+  int32_t n_slots;
+  k3moe* route;  // router over all E experts (its expert pointers are never read)
+  k3moe* arena;  // expert kernels over the n_slots arena slots
+  uint8_t* mem;  // arena: tensor t of slot s at dev[t] + s * bytes[t]
+  uint8_t* dev[kTensors];
+  const uint8_t* host[kTensors];
+  size_t bytes[kTensors];
+  size_t expert_total;
+  int32_t* idx_dev;    // [max_tokens][k] expert ids from the router
+  float* gate_dev;     // [max_tokens][k]
+  int32_t* sidx_dev;   // [max_tokens][k] the same selection as slot ids
+  int32_t* idx_host;   // pinned copies
+  int32_t* sidx_host;
+  std::vector<int32_t> slot_of;    // [E]: slot holding expert e, or -1
+  std::vector<int32_t> expert_in;  // [n_slots]: expert in slot s, or -1
+  std::vector<int64_t> last_use;   // [n_slots]: last call that used slot s (0: never)
+  std::vector<int64_t> seen;       // [E]: last call that routed to expert e
+  std::vector<int32_t> uniq;       // scratch: distinct experts of a call
+  int64_t calls, hits, misses, bytes_in;
+};
+
+namespace {
+
+struct Guard {
+  int prev = -1;
+  bool ok = false;
+  explicit Guard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~Guard() {
+    if (ok && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+void release(k3moe_cache* c) {
+  k3moe_destroy(c->route);
+  k3moe_destroy(c->arena);
+  (void)hipFree(c->mem);
+  (void)hipFree(c->idx_dev);
+  (void)hipFree(c->gate_dev);
+  (void)hipFree(c->sidx_dev);
+  (void)hipHostFree(c->idx_host);
+  (void)hipHostFree(c->sidx_host);
+}
+
+// Forget every resident expert (after a failed call the arena's contents are
+// not known).
+void forget(k3moe_cache* c) {
+  std::fill(c->slot_of.begin(), c->slot_of.end(), -1);
+  std::fill(c->expert_in.begin(), c->expert_in.end(), -1);
+  std::fill(c->last_use.begin(), c->last_use.end(), 0);
+}
+
+int fail(k3moe_cache* c, int rc) {
+  forget(c);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int32_t n_slots,
+                       int device, k3moe_cache** out) {
+  if (out) *out = nullptr;
+  if (!out || !w || !cfg) return K3MOE_EINVAL;
+  const int64_t ws = k3moe_workspace_bytes(cfg);  // validates cfg on the host
+  if (ws < 0) return (int)ws;
+  if (n_slots < cfg->top_k || n_slots > cfg->n_experts) return K3MOE_EINVAL;
+  if (!w->router_w || !aligned16(w->router_w)) return K3MOE_EINVAL;
+  if (w->router_b && !aligned16(w->router_b)) return K3MOE_EINVAL;
+  const uint8_t* hp[kTensors] = {w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const uint8_t* p : hp)
+    if (!p) return K3MOE_EINVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return K3MOE_EHIP;
+  if (device < 0 || device >= ndev) return K3MOE_EINVAL;
+  Guard guard(device);
+  if (!guard.ok) return K3MOE_EHIP;
+
+  k3moe_cache* c = new (std::nothrow) k3moe_cache();
+  if (!c) return K3MOE_ENOMEM;
+  c->cfg = *cfg;
+  c->device = device;
+  c->n_slots = n_slots;
+  expert_bytes(cfg, c->bytes);
+  c->expert_total = 0;
+  for (int t = 0; t < kTensors; ++t) {
+    c->host[t] = hp[t];
+    c->expert_total += c->bytes[t];  // each a multiple of 256 (1 KB code tiles, 256 B scale groups)
+  }
+  // arena: six tensors of n_slots experts, each tensor 256-byte aligned
+  size_t off[kTensors], total = 0;
+  for (int t = 0; t < kTensors; ++t) {
+    off[t] = total;
+    total += ((size_t)n_slots * c->bytes[t] + 255) / 256 * 256;
+  }
+  const size_t P = (size_t)cfg->max_tokens * cfg->top_k;
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+    delete c;
+    return K3MOE_EHIP;
+  }
+  // refuse before allocating: the arena, two workspaces, the selection buffers
+  if (total + 2 * (size_t)ws + 3 * P * 4 > free_b) {
+    delete c;
+    return K3MOE_ENOMEM;
+  }
+  void* m = nullptr;
+  bool ok = hipMalloc(&m, total) == hipSuccess;
+  c->mem = static_cast<uint8_t*>(m);
+  ok = ok && hipMalloc(reinterpret_cast<void**>(&c->idx_dev), P * 4) == hipSuccess;
+  ok = ok && hipMalloc(reinterpret_cast<void**>(&c->gate_dev), P * 4) == hipSuccess;
+  ok = ok && hipMalloc(reinterpret_cast<void**>(&c->sidx_dev), P * 4) == hipSuccess;
+  ok = ok && hipHostMalloc(reinterpret_cast<void**>(&c->idx_host), P * 4, 0) == hipSuccess;
+  ok = ok && hipHostMalloc(reinterpret_cast<void**>(&c->sidx_host), P * 4, 0) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    release(c);
+    delete c;
+    return K3MOE_ENOMEM;
+  }
+  for (int t = 0; t < kTensors; ++t) c->dev[t] = c->mem + off[t];
+  // the router handle sees all E experts; the arena handle sees the slots
+  k3moe_weights rw = {w->router_w, w->router_b, c->dev[0], c->dev[1], c->dev[2],
+                      c->dev[3],   c->dev[4],   c->dev[5]};
+  k3moe_config acfg = *cfg;
+  acfg.n_experts = n_slots;
+  int rc = k3moe_create(cfg, &rw, device, &c->route);
+  if (rc == K3MOE_OK) rc = k3moe_create(&acfg, &rw, device, &c->arena);
+  if (rc != K3MOE_OK) {
+    release(c);
+    delete c;
+    return rc;
+  }
+  c->slot_of.assign((size_t)cfg->n_experts, -1);
+  c->expert_in.assign((size_t)n_slots, -1);
+  c->last_use.assign((size_t)n_slots, 0);
+  c->seen.assign((size_t)cfg->n_experts, 0);
+  c->uniq.reserve((size_t)n_slots);
+  c->calls = c->hits = c->misses = c->bytes_in = 0;
+  *out = c;
+  return K3MOE_OK;
+}
+
+void k3moe_cache_destroy(k3moe_cache* c) {
+  if (!c) return;
+  {
+    Guard guard(c->device);
+    if (guard.ok) {
+      (void)hipDeviceSynchronize();
+      release(c);
+    }
+  }
+  delete c;
+}
+
+int k3moe_cache_stats(const k3moe_cache* c, int64_t* calls, int64_t* hits, int64_t* misses,
+                      int64_t* bytes_in) {
+  if (!c) return K3MOE_EINVAL;
+  if (calls) *calls = c->calls;
+  if (hits) *hits = c->hits;
+  if (misses) *misses = c->misses;
+  if (bytes_in) *bytes_in = c->bytes_in;
+  return K3MOE_OK;
+}
+
+int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int32_t* topk_idx,
+                        float* topk_gate, void* stream) {
+  if (!c) return K3MOE_EINVAL;
+  if (T < 0 || T > c->cfg.max_tokens) return K3MOE_EINVAL;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return K3MOE_EINVAL;
+  if ((topk_idx && (reinterpret_cast<uintptr_t>(topk_idx) & 3u)) ||
+      (topk_gate && (reinterpret_cast<uintptr_t>(topk_gate) & 3u)))
+    return K3MOE_EINVAL;
+  Guard guard(c->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t E = c->cfg.n_experts;
+  const size_t P = (size_t)T * c->cfg.top_k;
+
+  // 1. route over all experts and read the selection back
+  int rc = k3moe_route(c->route, x, T, nullptr, c->idx_dev, c->gate_dev, stream);
+  if (rc != K3MOE_OK) return fail(c, rc);
+  if (hipMemcpyAsync(c->idx_host, c->idx_dev, P * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, K3MOE_EHIP);
+  }
+
+  // 2. the call's distinct experts; refuse before changing anything if they
+  // cannot all be resident at once
+  const int64_t call = ++c->calls;
+  c->uniq.clear();
+  for (size_t p = 0; p < P; ++p) {
+    const int32_t e = c->idx_host[p];
+    if (e < 0 || e >= E || c->seen[(size_t)e] == call) continue;
+    c->seen[(size_t)e] = call;
+    if ((int32_t)c->uniq.size() == c->n_slots) return K3MOE_EUNSUPPORTED;
+    c->uniq.push_back(e);
+  }
+  // hits first, so no expert this call needs is evicted for another
+  for (int32_t e : c->uniq) {
+    const int32_t s = c->slot_of[(size_t)e];
+    if (s >= 0) {
+      c->last_use[(size_t)s] = call;
+      ++c->hits;
+    }
+  }
+  // 3. misses: the least recently used slot not used by this call (free
+  // slots have last_use 0); copy the expert in on the call's stream
+  for (int32_t e : c->uniq) {
+    if (c->slot_of[(size_t)e] >= 0) continue;
+    int32_t v = -1;
+    for (int32_t s = 0; s < c->n_slots; ++s)
+      if (c->last_use[(size_t)s] < call && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v]))
+        v = s;
+    // a victim exists: fewer distinct experts than slots are in use by this call
+    const int32_t old = c->expert_in[(size_t)v];
+    if (old >= 0) c->slot_of[(size_t)old] = -1;
+    for (int t = 0; t < kTensors; ++t) {
+      if (hipMemcpyAsync(c->dev[t] + (size_t)v * c->bytes[t], c->host[t] + (size_t)e * c->bytes[t],
+                         c->bytes[t], hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(c, K3MOE_EHIP);
+      }
+    }
+    c->expert_in[(size_t)v] = e;
+    c->slot_of[(size_t)e] = v;
+    c->last_use[(size_t)v] = call;
+    ++c->misses;
+    c->bytes_in += (int64_t)c->expert_total;
+  }
+  // 4. the selection renamed to slots (dropped pairs stay out of range)
+  for (size_t p = 0; p < P; ++p) {
+    const int32_t e = c->idx_host[p];
+    c->sidx_host[p] = (e >= 0 && e < E) ? c->slot_of[(size_t)e] : -1;
+  }
+  if (hipMemcpyAsync(c->sidx_dev, c->sidx_host, P * 4, hipMemcpyHostToDevice, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, K3MOE_EHIP);
+  }
+  // 5. the expert kernels over the arena
+  rc = k3moe_experts_forward(c->arena, x, T, c->sidx_dev, c->gate_dev, y, stream);
+  if (rc != K3MOE_OK) return fail(c, rc);
+  if ((topk_idx && hipMemcpyAsync(topk_idx, c->idx_dev, P * 4, hipMemcpyDeviceToDevice, st) !=
+                       hipSuccess) ||
+      (topk_gate && hipMemcpyAsync(topk_gate, c->gate_dev, P * 4, hipMemcpyDeviceToDevice, st) !=
+                        hipSuccess)) {
+    (void)hipGetLastError();
+    return fail(c, K3MOE_EHIP);
+  }
+  return K3MOE_OK;
+}
+
+}  // extern "C"

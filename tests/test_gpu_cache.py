@@ -1,0 +1,153 @@
+"""GPU tests of the HBM expert cache (k3moe_cache_*): expert weights in host
+memory, n_slots of them resident in HBM, replaced least-recently-used.
+
+The cached layer runs the same kernels on the same data as the all-resident
+layer, so its outputs must equal k3moe_layer_forward bit for bit; the hit and
+miss counts must follow the LRU rule exactly; and one output is checked
+against the C oracle as well."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._parity import check_output
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+EXPERT_TENSORS = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+
+
+@pytest.fixture(scope="module")
+def k3():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_expert_matmul_amd as k3m
+    k3m.load_library()
+    return k3m
+
+
+def _layers(k3, cfg, max_tokens, n_slots, bias=None):
+    from synth.device import host_weights_to_device
+    W = synth.gen_weights(cfg)
+    wr = synth.gen_router_w(cfg)
+    dw = k3.pack_layer_weights(host_weights_to_device(W, wr, bias), cfg.E, cfg.d, cfg.f)
+    host = {n: dw[n].cpu().pin_memory() for n in EXPERT_TENSORS}
+    host["router_w"] = dw["router_w"]
+    host["router_b"] = dw["router_b"]
+    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, max_tokens)
+    full = k3.Layer(c, dw, 0)
+    cached = k3.CachedLayer(c, host, n_slots, 0)
+    return W, wr, full, cached
+
+
+def _xd(x_bits):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("T", [1, 3, 12])
+def test_cached_equals_resident_layer(k3, T):
+    """Calls that hit, miss and evict give exactly the all-resident outputs
+    (GEMV path for T <= 4, grouped GEMM above)."""
+    cfg = synth.CONFIGS[1]  # 64 experts, top-8
+    n_slots = min(cfg.E, max(24, T * cfg.k))
+    _, _, full, cached = _layers(k3, cfg, 16, n_slots)
+    pool = synth.gen_x(cfg, T=T * 10, stream=10)
+    for i in range(10):
+        x = _xd(pool[i * T:(i + 1) * T])
+        y0, i0, g0 = full.forward(x)
+        y1, i1, g1 = cached.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(i0, i1) and torch.equal(g0, g1), f"call {i}: routing differs"
+        assert torch.equal(y0, y1), f"call {i}: output differs"
+    st = cached.stats()
+    assert st["calls"] == 10
+    assert st["misses"] > 0 and st["hits"] > 0
+    cached.close()
+    full.close()
+
+
+def test_lru_accounting(k3):
+    """Hit/miss counts against a host model of the LRU rule, with a cache
+    smaller than the experts the calls touch."""
+    cfg = synth.CONFIGS[1]
+    n_slots = 20
+    _, _, full, cached = _layers(k3, cfg, 4, n_slots)
+    pool = synth.gen_x(cfg, T=40, stream=11)
+    resident, last, hits, misses = {}, {}, 0, 0  # expert -> slot, slot -> last call
+    for call in range(1, 21):
+        x = _xd(pool[2 * (call - 1):2 * call])
+        _, idx, _ = cached.forward(x)
+        torch.cuda.synchronize()
+        uniq = list(dict.fromkeys(int(e) for e in idx.cpu().numpy().reshape(-1)))
+        for e in uniq:
+            if e in resident:
+                hits += 1
+                last[resident[e]] = call
+        for e in uniq:
+            if e in resident:
+                continue
+            free = [s for s in range(n_slots) if last.get(s, 0) < call]
+            v = min(free, key=lambda s: (last.get(s, 0), s))
+            for old, s in list(resident.items()):
+                if s == v:
+                    del resident[old]
+            resident[e] = v
+            last[v] = call
+            misses += 1
+    st = cached.stats()
+    assert (st["hits"], st["misses"]) == (hits, misses)
+    assert st["bytes_in"] == misses * cfg.expert_bytes()
+    cached.close()
+    full.close()
+
+
+def test_cached_layer_against_oracle(k3):
+    cfg = synth.CONFIGS[1]
+    W, wr, full, cached = _layers(k3, cfg, 8, 16)
+    x = synth.gen_x(cfg, T=2, stream=12)
+    for _ in range(2):  # the second call hits
+        y, idx, gate = cached.forward(_xd(x))
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(x, wr, None, synth.ExpertSource(cfg, W), cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    check_output(y.cpu().numpy(), ref["y64"], "cached layer")
+    cached.close()
+    full.close()
+
+
+def test_too_many_distinct_experts_is_refused(k3):
+    """A call that routes to more distinct experts than there are slots is
+    refused after routing, before any expert is copied or computed; the
+    cache keeps working afterwards."""
+    cfg = synth.CONFIGS[1]
+    _, _, full, cached = _layers(k3, cfg, 16, 8)  # 8 slots, top-8
+    x = synth.gen_x(cfg, T=16, stream=13)
+    with pytest.raises(k3.K3MoEError) as ei:
+        cached.forward(_xd(x))
+    assert ei.value.status == k3.K3MOE_EUNSUPPORTED
+    y0, _, _ = full.forward(_xd(x[:1]))
+    y1, _, _ = cached.forward(_xd(x[:1]))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    cached.close()
+    full.close()
+
+
+def test_cache_create_rejects_bad_arguments(k3):
+    cfg = synth.CONFIGS[1]
+    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, 4)
+    host = {n: torch.zeros(16, dtype=torch.uint8) for n in EXPERT_TENSORS}
+    host["router_w"] = torch.zeros((cfg.E, cfg.d), dtype=torch.float32, device="cuda")
+    for n_slots in (cfg.k - 1, cfg.E + 1):  # fewer slots than top-k, more than experts
+        with pytest.raises(k3.K3MoEError) as ei:
+            k3.CachedLayer(c, host, n_slots, 0)
+        assert ei.value.status == k3.K3MOE_EINVAL
+    bad = dict(host)
+    bad["down_s"] = None
+    with pytest.raises(k3.K3MoEError) as ei:
+        k3.CachedLayer(c, bad, 16, 0)
+    assert ei.value.status == k3.K3MOE_EINVAL
