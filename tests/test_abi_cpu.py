@@ -74,3 +74,26 @@ def test_create_without_gpu_returns_status(lib):
     with pytest.raises(lib.K3MoEError) as ei:
         lib.Layer(lib.Config(128, 8, 2, 256, 1), {}, 0)
     assert ei.value.status in (lib.K3MOE_EINVAL, lib.K3MOE_EHIP)
+
+
+def test_cache_create_validates_before_any_device_call(lib):
+    """k3moe_cache_create checks its arguments on the host first: these
+    calls return their status without touching a GPU."""
+    import ctypes as C
+    from mxfp4_expert_matmul_amd._binding import _Weights
+    dll = lib.load_library()
+    out = C.c_void_p()
+    good = lib.Config(2048, 64, 8, 1024, 4)._c()
+    buf = (C.c_uint8 * 64)()
+    p = C.cast(C.addressof(buf) + (-C.addressof(buf)) % 16, C.c_void_p).value  # 16-byte aligned
+    w = _Weights(p, None, p, p, p, p, p, p)
+    assert dll.k3moe_cache_create(C.byref(good), None, 16, 0, C.byref(out)) == lib.K3MOE_EINVAL
+    for n_slots in (7, 65):  # fewer than top-k, more than the experts
+        assert dll.k3moe_cache_create(C.byref(good), C.byref(w), n_slots, 0, C.byref(out)) == lib.K3MOE_EINVAL
+    bad = lib.Config(160, 64, 8, 1024, 4)._c()  # d % 128 != 0
+    assert dll.k3moe_cache_create(C.byref(bad), C.byref(w), 16, 0, C.byref(out)) == lib.K3MOE_EUNSUPPORTED
+    nodown = _Weights(p, None, p, p, p, p, p, None)
+    assert dll.k3moe_cache_create(C.byref(good), C.byref(nodown), 16, 0, C.byref(out)) == lib.K3MOE_EINVAL
+    assert out.value is None
+    assert dll.k3moe_cache_stats(None, None, None, None, None) == lib.K3MOE_EINVAL
+    dll.k3moe_cache_destroy(None)  # NULL-safe
