@@ -233,8 +233,9 @@ int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int
 int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int32_t* topk_idx,
                         float* topk_gate, void* stream);
 
-/* Counters since create (HOST outputs, any may be NULL): calls, distinct
- * experts found resident (hits) and copied in (misses), and bytes copied. */
+/* Counters since create (HOST outputs, any may be NULL): completed calls,
+ * distinct experts found resident (hits) and copied in (misses) per call,
+ * and bytes copied. A refused call counts nowhere. */
 int k3moe_cache_stats(const k3moe_cache* c, int64_t* calls, int64_t* hits, int64_t* misses,
                       int64_t* bytes_in);
 

@@ -56,10 +56,11 @@ struct k3moe_cache {
   int32_t* sidx_host;
   std::vector<int32_t> slot_of;    // [E]: slot holding expert e, or -1
   std::vector<int32_t> expert_in;  // [n_slots]: expert in slot s, or -1
-  std::vector<int64_t> last_use;   // [n_slots]: last call that used slot s (0: never)
-  std::vector<int64_t> seen;       // [E]: last call that routed to expert e
+  std::vector<int64_t> last_use;   // [n_slots]: stamp of the last call that used slot s (0: never)
+  std::vector<int64_t> seen;       // [E]: stamp of the last call that routed to expert e
   std::vector<int32_t> uniq;       // scratch: distinct experts of a call
-  int64_t calls, hits, misses, bytes_in;
+  int64_t stamp;                   // counts every call that got past the routing
+  int64_t calls, hits, misses, bytes_in;  // completed calls and their experts
 };
 
 namespace {
@@ -182,7 +183,7 @@ int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int
   c->last_use.assign((size_t)n_slots, 0);
   c->seen.assign((size_t)cfg->n_experts, 0);
   c->uniq.reserve((size_t)n_slots);
-  c->calls = c->hits = c->misses = c->bytes_in = 0;
+  c->stamp = c->calls = c->hits = c->misses = c->bytes_in = 0;
   *out = c;
   return K3MOE_OK;
 }
@@ -235,7 +236,7 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
 
   // 2. the call's distinct experts; refuse before changing anything if they
   // cannot all be resident at once
-  const int64_t call = ++c->calls;
+  const int64_t call = ++c->stamp;
   c->uniq.clear();
   for (size_t p = 0; p < P; ++p) {
     const int32_t e = c->idx_host[p];
@@ -244,12 +245,13 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     if ((int32_t)c->uniq.size() == c->n_slots) return K3MOE_EUNSUPPORTED;
     c->uniq.push_back(e);
   }
+  int64_t hits = 0, misses = 0;
   // hits first, so no expert this call needs is evicted for another
   for (int32_t e : c->uniq) {
     const int32_t s = c->slot_of[(size_t)e];
     if (s >= 0) {
       c->last_use[(size_t)s] = call;
-      ++c->hits;
+      ++hits;
     }
   }
   // 3. misses: the least recently used slot not used by this call (free
@@ -273,8 +275,7 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     c->expert_in[(size_t)v] = e;
     c->slot_of[(size_t)e] = v;
     c->last_use[(size_t)v] = call;
-    ++c->misses;
-    c->bytes_in += (int64_t)c->expert_total;
+    ++misses;
   }
   // 4. the selection renamed to slots (dropped pairs stay out of range)
   for (size_t p = 0; p < P; ++p) {
@@ -295,6 +296,10 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     (void)hipGetLastError();
     return fail(c, K3MOE_EHIP);
   }
+  ++c->calls;
+  c->hits += hits;
+  c->misses += misses;
+  c->bytes_in += misses * (int64_t)c->expert_total;
   return K3MOE_OK;
 }
 

@@ -129,6 +129,7 @@ def test_too_many_distinct_experts_is_refused(k3):
     with pytest.raises(k3.K3MoEError) as ei:
         cached.forward(_xd(x))
     assert ei.value.status == k3.K3MOE_EUNSUPPORTED
+    assert cached.stats() == {"calls": 0, "hits": 0, "misses": 0, "bytes_in": 0}
     y0, _, _ = full.forward(_xd(x[:1]))
     y1, _, _ = cached.forward(_xd(x[:1]))
     torch.cuda.synchronize()
