@@ -54,7 +54,7 @@ extern "C" {
 #define K3MOE_EINVAL        -1   /* bad argument: null pointer, bad size, misalignment */
 #define K3MOE_ENOMEM        -2   /* device memory for the workspace is not available */
 #define K3MOE_EHIP          -3   /* a HIP runtime call or kernel launch failed */
-#define K3MOE_EUNSUPPORTED  -4   /* valid but outside what this build supports */
+#define K3MOE_EUNSUPPORTED  -4   /* valid but outside what the library supports */
 
 typedef struct k3moe k3moe;  /* opaque handle */
 

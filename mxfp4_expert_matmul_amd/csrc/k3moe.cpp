@@ -247,7 +247,7 @@ const char* k3moe_status_str(int status) {
     case K3MOE_EINVAL: return "invalid argument";
     case K3MOE_ENOMEM: return "not enough device memory for the workspace";
     case K3MOE_EHIP: return "HIP runtime or kernel launch failure";
-    case K3MOE_EUNSUPPORTED: return "configuration not supported by this build";
+    case K3MOE_EUNSUPPORTED: return "configuration outside what the library supports";
     default: return "unknown status";
   }
 }
