@@ -152,3 +152,35 @@ def test_cache_create_rejects_bad_arguments(k3):
     with pytest.raises(k3.K3MoEError) as ei:
         k3.CachedLayer(c, bad, 16, 0)
     assert ei.value.status == k3.K3MOE_EINVAL
+
+
+@pytest.mark.timeout(600)
+def test_cached_k3_decode_equals_resident(k3):
+    """K3 shape (896 experts, 21 GB of MXFP4 experts in pinned host memory)
+    behind a 64-slot arena: decode steps that miss and evict give exactly the
+    resident layer's outputs."""
+    from synth.device import device_weights, device_x
+    cfg = synth.CONFIGS[2]
+    dw = device_weights(cfg, torch.device("cuda:0"))
+    host = {}
+    for n in EXPERT_TENSORS:
+        h = torch.empty(dw[n].numel(), dtype=torch.uint8, pin_memory=True)
+        h.copy_(dw[n].view(-1))
+        host[n] = h
+    host["router_w"] = dw["router_w"]
+    host["router_b"] = dw.get("router_b")
+    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, 1)
+    full = k3.Layer(c, dw, 0)
+    cached = k3.CachedLayer(c, host, 64, 0)
+    xp = device_x(cfg, T=8, stream=10, device=torch.device("cuda:0"))
+    for i in range(8):
+        y0, i0, _ = full.forward(xp[i:i + 1])
+        y1, i1, _ = cached.forward(xp[i:i + 1])
+        torch.cuda.synchronize()
+        assert torch.equal(i0, i1) and torch.equal(y0, y1), f"token {i}"
+    st = cached.stats()
+    assert st["calls"] == 8 and st["misses"] >= 64  # the arena was refilled
+    cached.close()
+    full.close()
+    del dw, host
+    torch.cuda.empty_cache()
