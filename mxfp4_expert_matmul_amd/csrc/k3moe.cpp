@@ -132,6 +132,10 @@ struct k3moe {
   int prof_cap;
   int prof_n[K3MOE_NUM_STAGES];
   std::vector<hipEvent_t> prof_ev[K3MOE_NUM_STAGES];  // 2 per recorded launch
+  // a second stream (default priority) on which the whole-layer call splits x
+  // for the prefill GEMM while the router runs on the caller's stream
+  hipStream_t side;
+  hipEvent_t ev_fork, ev_join;
 };
 
 namespace {
@@ -192,7 +196,7 @@ int run_router(k3moe* h, const uint16_t* x, int T, float* logits, int32_t* idx, 
 // gate/up GEMV selects each token's experts itself and writes idx and gate;
 // otherwise idx and gate are the routing and are only read.
 int run_experts(k3moe* h, const uint16_t* x, int T, int32_t* idx, float* gate, float* y,
-                hipStream_t st, const float* logits = nullptr) {
+                hipStream_t st, const float* logits = nullptr, bool x_split_on_side = false) {
   const Shape s = shape_of(h);
   const k3::ExpertWeights w = experts_of(h);
   hipError_t e;
@@ -210,8 +214,13 @@ int run_experts(k3moe* h, const uint16_t* x, int T, int32_t* idx, float* gate, f
                             h->ntiles, st);
   });
   if (e != hipSuccess) return K3MOE_EHIP;
-  e = stage(h, K3MOE_STAGE_QUANT_X, st,
-            [&] { return k3::launch_quant_x(x, T, s.d, h->xq, h->xs, st); });
+  if (x_split_on_side) {
+    // the split of x was enqueued on the side stream before the router
+    e = hipStreamWaitEvent(st, h->ev_join, 0);
+  } else {
+    e = stage(h, K3MOE_STAGE_QUANT_X, st,
+              [&] { return k3::launch_quant_x(x, T, s.d, h->xq, h->xs, st); });
+  }
   if (e != hipSuccess) return K3MOE_EHIP;
   // the tile bound for this call's T (never above the workspace's)
   const size_t P = (size_t)T * s.k;
@@ -324,8 +333,13 @@ int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3
   if (k3::prepare_gemv(shape_of(h)) != hipSuccess ||
       k3::launch_router_split(w->router_w, cfg->n_experts, cfg->d_model, h->wr3, nullptr) !=
           hipSuccess ||
-      hipStreamSynchronize(nullptr) != hipSuccess) {
+      hipStreamSynchronize(nullptr) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->side) (void)hipStreamDestroy(h->side);
     (void)hipFree(h->ws);
     delete h;
     return K3MOE_EHIP;
@@ -341,6 +355,9 @@ void k3moe_destroy(k3moe* h) {
     if (guard.ok) {
       (void)hipDeviceSynchronize();
       profile_release(h);
+      (void)hipEventDestroy(h->ev_join);
+      (void)hipEventDestroy(h->ev_fork);
+      (void)hipStreamDestroy(h->side);
       (void)hipFree(h->ws);
     }
   }
@@ -409,11 +426,27 @@ int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y, int32_t* t
   float* gate = topk_gate ? topk_gate : h->gate;
   // few tokens: the gate/up GEMV does the top-k selection (one launch fewer)
   const bool fused_topk = T <= k3::kGemvMaxT;
-  int rc2 = run_router(h, static_cast<const uint16_t*>(x), T, h->logits, idx, gate, st,
-                       !fused_topk);
-  if (rc2 != K3MOE_OK) return rc2;
-  return run_experts(h, static_cast<const uint16_t*>(x), T, idx, gate, y, st,
-                     fused_topk ? h->logits : nullptr);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (!fused_topk) {
+    // the split of x for the prefill GEMM needs only x: it runs on the side
+    // stream, after everything already on the caller's stream, while the
+    // router runs (the router leaves CUs idle at large T); the gate/up GEMM
+    // waits for it
+    const Shape s = shape_of(h);
+    hipError_t e = hipEventRecord(h->ev_fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->ev_fork, 0);
+    if (e == hipSuccess)
+      e = stage(h, K3MOE_STAGE_QUANT_X, h->side,
+                [&] { return k3::launch_quant_x(xb, T, s.d, h->xq, h->xs, h->side); });
+    if (e == hipSuccess) e = hipEventRecord(h->ev_join, h->side);
+    if (e != hipSuccess) return K3MOE_EHIP;
+  }
+  int rc2 = run_router(h, xb, T, h->logits, idx, gate, st, !fused_topk);
+  if (rc2 != K3MOE_OK) {
+    if (!fused_topk) (void)hipStreamWaitEvent(st, h->ev_join, 0);  // keep the side joined
+    return rc2;
+  }
+  return run_experts(h, xb, T, idx, gate, y, st, fused_topk ? h->logits : nullptr, !fused_topk);
 }
 
 
