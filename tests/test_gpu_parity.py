@@ -262,15 +262,10 @@ def test_batch_invariance(k3):
     layer.close()
 
 
-@pytest.mark.parametrize("T", [1, 3, 40])
-def test_graph_replay_matches_eager(k3, T):
-    """Forwards captured in one HIP graph (each with its own input and output
-    buffers) and replayed three times, with eager forwards of the same layer
-    in between, give exactly the eager outputs on every replay (decode GEMV
-    path for T <= 4, grouped path above: both deterministic)."""
-    cfg = synth.CONFIGS[1]
-    s = Small(cfg, 64)
-    layer = _layer(k3, cfg, s.dw, 64)
+def _check_graph_replay(k3, layer, cfg, T):
+    """Three forwards captured in one HIP graph (each with its own input and
+    output buffers) and replayed three times, with eager forwards of the same
+    layer in between, give exactly the eager outputs on every replay."""
     xs = [_x_dev(synth.gen_x(cfg, T=T, stream=10 + i)) for i in range(3)]
     outs = [(torch.empty((T, cfg.d), dtype=torch.float32, device="cuda"),
              torch.empty((T, cfg.k), dtype=torch.int32, device="cuda"),
@@ -298,6 +293,16 @@ def test_graph_replay_matches_eager(k3, T):
             assert torch.equal(i, ri) and torch.equal(g, rg), f"replay {rep}: routing differs"
             assert torch.equal(y, ry), f"replay {rep}: output differs"
     del graph
+
+
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_graph_replay_matches_eager(k3, T):
+    """Graph replay equals eager (decode GEMV path for T <= 4, grouped path
+    above: both deterministic)."""
+    cfg = synth.CONFIGS[1]
+    s = Small(cfg, 64)
+    layer = _layer(k3, cfg, s.dw, 64)
+    _check_graph_replay(k3, layer, cfg, T)
     layer.close()
 
 
@@ -470,6 +475,31 @@ def test_k3_decode(k3, big_layers):
     cfg = st["cfg"]
     x = synth.gen_x(cfg)
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], label="k3 decode")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T", [4, 16])
+def test_k3_small_batches(k3, big_layers, T):
+    """A few tokens at the K3 shape (speculative-verify and multi-sequence
+    decode batches): T = 4 runs the GEMV path with several tokens, T = 16 the
+    grouped GEMM with one or two tokens per expert tile. Every token is
+    checked; the tokens follow the decode token in the seeded stream."""
+    _say(f"case k3 small batch T={T}")
+    st = big_layers(2, 4096)
+    cfg = st["cfg"]
+    x = synth.gen_x(cfg, T=T, start_token=1)
+    _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"],
+                   label=f"k3 small batch T={T}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T", [1, 16])
+def test_k3_graph_replay(k3, big_layers, T):
+    """At the K3 shape, graph replay (how decode steps are timed) equals eager
+    on every replay."""
+    _say(f"case k3 graph replay T={T}")
+    st = big_layers(2, 4096)
+    _check_graph_replay(k3, st["layer"], st["cfg"], T)
 
 
 @pytest.mark.timeout(600)
