@@ -194,8 +194,10 @@ int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K);
  * expert kernels on the arena with the selection renamed to slots. Results
  * equal k3moe_layer_forward on the same weights bit for bit (the same
  * kernels on the same data; only the place of the weights differs).
- * There is no prefetch: every hit is on an expert resident before the call,
- * so the raw and the true resident hit rates coincide. */
+ * k3moe_cache_prefetch copies experts in ahead of the call that needs them
+ * (the pages' prefetcher, for instance on a copy stream while the previous
+ * call computes). A hit on such an expert is a raw hit but not a true
+ * resident one, so the two rates differ by the prefetch hits. */
 typedef struct k3moe_cache k3moe_cache;
 
 /* Host-resident expert weights of a cached layer (HOST struct).
@@ -234,10 +236,30 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
                         float* topk_gate, void* stream);
 
 /* Counters since create (HOST outputs, any may be NULL): completed calls,
- * distinct experts found resident (hits) and copied in (misses) per call,
- * and bytes copied. A refused call counts nowhere. */
+ * distinct experts found resident (hits, raw: prefetched ones included) and
+ * copied in (misses) per call, and bytes copied by calls and prefetches. A
+ * refused call counts nowhere. */
 int k3moe_cache_stats(const k3moe_cache* c, int64_t* calls, int64_t* hits, int64_t* misses,
                       int64_t* bytes_in);
+
+/* Prefetch: copy the listed experts (HOST array of n expert ids, repeats
+ * allowed; n = 0 does nothing) that are not resident into the arena, on
+ * `stream` (hipStream_t, NULL = default stream), and refresh the resident
+ * ones in the LRU order. The copies go into the least recently used slots
+ * that the last forward does not use (its kernels may still run), so a
+ * prefetch may be issued on another stream while that forward computes. The
+ * next k3moe_cache_forward waits for the copies before it copies into or
+ * reads any slot. Prefetches must use one stream (or be ordered by the
+ * caller). Errors: K3MOE_EINVAL for a NULL cache, n < 0 or an id outside
+ * [0, E); K3MOE_EUNSUPPORTED, with nothing changed, if more experts need a
+ * slot than such slots exist; K3MOE_EHIP if a copy cannot be enqueued (the
+ * cache then forgets every resident expert). */
+int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void* stream);
+
+/* Prefetch counters (HOST outputs, any may be NULL): experts copied in by
+ * prefetches, and hits of completed calls on experts a prefetch brought in
+ * and no call had used before. True resident hits = hits - prefetch_hits. */
+int k3moe_cache_prefetch_stats(const k3moe_cache* c, int64_t* prefetched, int64_t* prefetch_hits);
 
 /* Destroy: synchronises the device, frees the arena and both handles.
  * NULL-safe; never frees the weights. */

@@ -102,6 +102,10 @@ def load_library():
     lib.k3moe_cache_stats.restype = ctypes.c_int
     lib.k3moe_cache_destroy.argtypes = [vp]
     lib.k3moe_cache_destroy.restype = None
+    lib.k3moe_cache_prefetch.argtypes = [vp, vp, i32, vp]
+    lib.k3moe_cache_prefetch.restype = ctypes.c_int
+    lib.k3moe_cache_prefetch_stats.argtypes = [vp, vp, vp]
+    lib.k3moe_cache_prefetch_stats.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -265,11 +269,28 @@ class CachedLayer:
                "k3moe_cache_forward")
         return y, idx, gate
 
+    def prefetch(self, experts, stream=None, device: int = 0):
+        """Copy the listed experts (host ints) into the arena on `stream`
+        (torch stream or None for the current one); the next forward waits
+        for the copies."""
+        import torch
+        ids = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+        _check(load_library().k3moe_cache_prefetch(self.handle, ids, len(experts),
+                                                   _stream(stream, torch.device("cuda", device))),
+               "k3moe_cache_prefetch")
+
     def stats(self) -> dict:
-        v = [ctypes.c_int64() for _ in range(4)]
-        _check(load_library().k3moe_cache_stats(self.handle, *[ctypes.byref(a) for a in v]),
+        """calls, hits (raw: including experts a prefetch brought in), misses,
+        bytes_in (forwards and prefetches), prefetched and prefetch_hits; true
+        resident hits are hits - prefetch_hits."""
+        lib = load_library()
+        v = [ctypes.c_int64() for _ in range(6)]
+        _check(lib.k3moe_cache_stats(self.handle, *[ctypes.byref(a) for a in v[:4]]),
                "k3moe_cache_stats")
-        return dict(zip(("calls", "hits", "misses", "bytes_in"), (a.value for a in v)))
+        _check(lib.k3moe_cache_prefetch_stats(self.handle, *[ctypes.byref(a) for a in v[4:]]),
+               "k3moe_cache_prefetch_stats")
+        return dict(zip(("calls", "hits", "misses", "bytes_in", "prefetched", "prefetch_hits"),
+                        (a.value for a in v)))
 
     def close(self):
         if self.handle:

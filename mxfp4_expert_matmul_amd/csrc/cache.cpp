@@ -58,9 +58,15 @@ struct k3moe_cache {
   std::vector<int32_t> expert_in;  // [n_slots]: expert in slot s, or -1
   std::vector<int64_t> last_use;   // [n_slots]: stamp of the last call that used slot s (0: never)
   std::vector<int64_t> seen;       // [E]: stamp of the last call that routed to expert e
+  std::vector<int64_t> fwd_use;    // [n_slots]: stamp of the last forward that used slot s
+  std::vector<uint8_t> pre;        // [n_slots]: brought in by a prefetch, not used since
   std::vector<int32_t> uniq;       // scratch: distinct experts of a call
-  int64_t stamp;                   // counts every call that got past the routing
+  int64_t stamp;                   // counts every forward past the routing and every prefetch
+  int64_t last_fwd;                // stamp of the last forward that enqueued its kernels (0: none)
+  hipEvent_t pf_ev;                // recorded after the last prefetch's copies
+  bool pf_pending;                 // the next forward must wait for pf_ev
   int64_t calls, hits, misses, bytes_in;  // completed calls and their experts
+  int64_t prefetched, pf_hits;     // experts copied by prefetches; hits on them
 };
 
 namespace {
@@ -78,6 +84,7 @@ struct Guard {
 };
 
 void release(k3moe_cache* c) {
+  if (c->pf_ev) (void)hipEventDestroy(c->pf_ev);
   k3moe_destroy(c->route);
   k3moe_destroy(c->arena);
   (void)hipFree(c->mem);
@@ -94,6 +101,27 @@ void forget(k3moe_cache* c) {
   std::fill(c->slot_of.begin(), c->slot_of.end(), -1);
   std::fill(c->expert_in.begin(), c->expert_in.end(), -1);
   std::fill(c->last_use.begin(), c->last_use.end(), 0);
+  std::fill(c->pre.begin(), c->pre.end(), 0);
+}
+
+// Copy expert e into slot v on stream st (the six tensors); the caller
+// updates the residency tables.
+hipError_t copy_in(k3moe_cache* c, int32_t e, int32_t v, hipStream_t st) {
+  for (int t = 0; t < kTensors; ++t) {
+    const hipError_t r =
+        hipMemcpyAsync(c->dev[t] + (size_t)v * c->bytes[t], c->host[t] + (size_t)e * c->bytes[t],
+                       c->bytes[t], hipMemcpyHostToDevice, st);
+    if (r != hipSuccess) return r;
+  }
+  return hipSuccess;
+}
+
+// Put expert e in slot v (evicting what v held).
+void place(k3moe_cache* c, int32_t e, int32_t v) {
+  const int32_t old = c->expert_in[(size_t)v];
+  if (old >= 0) c->slot_of[(size_t)old] = -1;
+  c->expert_in[(size_t)v] = e;
+  c->slot_of[(size_t)e] = v;
 }
 
 int fail(k3moe_cache* c, int rc) {
@@ -183,7 +211,18 @@ int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int
   c->last_use.assign((size_t)n_slots, 0);
   c->seen.assign((size_t)cfg->n_experts, 0);
   c->uniq.reserve((size_t)n_slots);
+  c->fwd_use.assign((size_t)n_slots, 0);
+  c->pre.assign((size_t)n_slots, 0);
   c->stamp = c->calls = c->hits = c->misses = c->bytes_in = 0;
+  c->last_fwd = c->prefetched = c->pf_hits = 0;
+  c->pf_pending = false;
+  if (hipEventCreateWithFlags(&c->pf_ev, hipEventDisableTiming) != hipSuccess) {
+    c->pf_ev = nullptr;
+    (void)hipGetLastError();
+    release(c);
+    delete c;
+    return K3MOE_EHIP;
+  }
   *out = c;
   return K3MOE_OK;
 }
@@ -245,13 +284,23 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     if ((int32_t)c->uniq.size() == c->n_slots) return K3MOE_EUNSUPPORTED;
     c->uniq.push_back(e);
   }
-  int64_t hits = 0, misses = 0;
+  // copies of an earlier prefetch (possibly on another stream) land before
+  // this call copies into, or reads, any slot
+  if (c->pf_pending) {
+    if (hipStreamWaitEvent(st, c->pf_ev, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(c, K3MOE_EHIP);
+    }
+    c->pf_pending = false;
+  }
+  int64_t hits = 0, misses = 0, pf_hits = 0;
   // hits first, so no expert this call needs is evicted for another
   for (int32_t e : c->uniq) {
     const int32_t s = c->slot_of[(size_t)e];
     if (s >= 0) {
       c->last_use[(size_t)s] = call;
       ++hits;
+      pf_hits += c->pre[(size_t)s];
     }
   }
   // 3. misses: the least recently used slot not used by this call (free
@@ -263,20 +312,22 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
       if (c->last_use[(size_t)s] < call && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v]))
         v = s;
     // a victim exists: fewer distinct experts than slots are in use by this call
-    const int32_t old = c->expert_in[(size_t)v];
-    if (old >= 0) c->slot_of[(size_t)old] = -1;
-    for (int t = 0; t < kTensors; ++t) {
-      if (hipMemcpyAsync(c->dev[t] + (size_t)v * c->bytes[t], c->host[t] + (size_t)e * c->bytes[t],
-                         c->bytes[t], hipMemcpyHostToDevice, st) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(c, K3MOE_EHIP);
-      }
+    place(c, e, v);
+    if (copy_in(c, e, v, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(c, K3MOE_EHIP);
     }
-    c->expert_in[(size_t)v] = e;
-    c->slot_of[(size_t)e] = v;
     c->last_use[(size_t)v] = call;
     ++misses;
   }
+  // every slot this call uses: a plain resident from now on, and off limits
+  // to prefetches until a later forward is enqueued
+  for (int32_t e : c->uniq) {
+    const int32_t s = c->slot_of[(size_t)e];
+    c->pre[(size_t)s] = 0;
+    c->fwd_use[(size_t)s] = call;
+  }
+  c->last_fwd = call;
   // 4. the selection renamed to slots (dropped pairs stay out of range)
   for (size_t p = 0; p < P; ++p) {
     const int32_t e = c->idx_host[p];
@@ -299,7 +350,71 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
   ++c->calls;
   c->hits += hits;
   c->misses += misses;
+  c->pf_hits += pf_hits;
   c->bytes_in += misses * (int64_t)c->expert_total;
+  return K3MOE_OK;
+}
+
+int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void* stream) {
+  if (!c || n < 0 || (n > 0 && !experts)) return K3MOE_EINVAL;
+  const int32_t E = c->cfg.n_experts;
+  for (int32_t i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= E) return K3MOE_EINVAL;
+  if (n == 0) return K3MOE_OK;
+  Guard guard(c->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t pst = ++c->stamp;
+  // distinct listed experts; resident ones are refreshed, the rest need slots
+  c->uniq.clear();
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t e = experts[i];
+    if (c->seen[(size_t)e] == pst) continue;
+    c->seen[(size_t)e] = pst;
+    if (c->slot_of[(size_t)e] < 0) c->uniq.push_back(e);
+  }
+  // slots a prefetch may fill: not used by the last forward (its kernels may
+  // still run) and not taken by this prefetch; refuse before changing anything
+  // if there are too few
+  auto eligible = [&](int32_t s) {
+    return (c->last_fwd == 0 || c->fwd_use[(size_t)s] != c->last_fwd) && c->last_use[(size_t)s] < pst;
+  };
+  int32_t free_slots = 0;
+  for (int32_t s = 0; s < c->n_slots; ++s) free_slots += eligible(s) ? 1 : 0;
+  if ((int32_t)c->uniq.size() > free_slots) return K3MOE_EUNSUPPORTED;
+  for (int32_t i = 0; i < n; ++i) {  // refresh the resident ones
+    const int32_t s = c->slot_of[(size_t)experts[i]];
+    if (s >= 0 && eligible(s)) c->last_use[(size_t)s] = pst;
+  }
+  int64_t copied = 0;
+  for (int32_t e : c->uniq) {
+    int32_t v = -1;
+    for (int32_t s = 0; s < c->n_slots; ++s)
+      if (eligible(s) && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v])) v = s;
+    place(c, e, v);
+    if (copy_in(c, e, v, st) != hipSuccess) {
+      (void)hipGetLastError();
+      c->pf_pending = false;
+      return fail(c, K3MOE_EHIP);
+    }
+    c->last_use[(size_t)v] = pst;
+    c->pre[(size_t)v] = 1;
+    ++copied;
+  }
+  if (hipEventRecord(c->pf_ev, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, K3MOE_EHIP);
+  }
+  c->pf_pending = true;
+  c->prefetched += copied;
+  c->bytes_in += copied * (int64_t)c->expert_total;
+  return K3MOE_OK;
+}
+
+int k3moe_cache_prefetch_stats(const k3moe_cache* c, int64_t* prefetched, int64_t* prefetch_hits) {
+  if (!c) return K3MOE_EINVAL;
+  if (prefetched) *prefetched = c->prefetched;
+  if (prefetch_hits) *prefetch_hits = c->pf_hits;
   return K3MOE_OK;
 }
 

@@ -129,7 +129,8 @@ def test_too_many_distinct_experts_is_refused(k3):
     with pytest.raises(k3.K3MoEError) as ei:
         cached.forward(_xd(x))
     assert ei.value.status == k3.K3MOE_EUNSUPPORTED
-    assert cached.stats() == {"calls": 0, "hits": 0, "misses": 0, "bytes_in": 0}
+    assert cached.stats() == {"calls": 0, "hits": 0, "misses": 0, "bytes_in": 0,
+                              "prefetched": 0, "prefetch_hits": 0}
     y0, _, _ = full.forward(_xd(x[:1]))
     y1, _, _ = cached.forward(_xd(x[:1]))
     torch.cuda.synchronize()
@@ -184,3 +185,74 @@ def test_cached_k3_decode_equals_resident(k3):
     full.close()
     del dw, host
     torch.cuda.empty_cache()
+
+
+def test_prefetch_ahead_on_a_copy_stream(k3):
+    """Each call's experts are prefetched on a second stream right after the
+    previous call is enqueued (its kernels may still run). Outputs equal the
+    resident layer bit for bit. After the first call nothing is missed, every
+    prefetched expert is a prefetch hit, and raw hits (all) exceed true
+    resident hits (hits minus prefetch hits) by exactly those."""
+    cfg = synth.CONFIGS[1]  # 64 experts, top-8
+    T, n_calls = 2, 12
+    _, _, full, cached = _layers(k3, cfg, 8, 40)
+    pool = synth.gen_x(cfg, T=T * n_calls, stream=14)
+    xs = [_xd(pool[i * T:(i + 1) * T]) for i in range(n_calls)]
+    refs = [full.forward(x) for x in xs]  # reference outputs and each call's routing
+    torch.cuda.synchronize()
+    copy = torch.cuda.Stream()
+    y, idx, _ = cached.forward(xs[0])
+    torch.cuda.synchronize()
+    assert torch.equal(y, refs[0][0]) and torch.equal(idx, refs[0][1])
+    prev = cached.stats()
+    for n in range(1, n_calls):
+        experts = refs[n][1].cpu().numpy().reshape(-1).tolist()
+        cached.prefetch(experts, stream=copy)
+        y, idx, gate = cached.forward(xs[n])
+        torch.cuda.synchronize()
+        assert torch.equal(idx, refs[n][1]) and torch.equal(gate, refs[n][2]), f"call {n}"
+        assert torch.equal(y, refs[n][0]), f"call {n}: output differs"
+        st = cached.stats()
+        new = st["prefetched"] - prev["prefetched"]
+        assert st["misses"] == prev["misses"], f"call {n}: a prefetched expert was missed"
+        assert st["hits"] - prev["hits"] == len(set(experts))
+        assert st["prefetch_hits"] - prev["prefetch_hits"] == new
+        assert st["bytes_in"] - prev["bytes_in"] == new * cfg.expert_bytes()
+        prev = st
+    assert prev["prefetched"] > 0 and prev["hits"] - prev["prefetch_hits"] > 0
+    cached.close()
+    full.close()
+
+
+def test_prefetch_refusals(k3):
+    """Invalid ids are refused; an empty list does nothing; a prefetch that
+    needs more slots than those the last call leaves free is refused with
+    nothing changed, and the cache keeps working."""
+    cfg = synth.CONFIGS[1]
+    n_slots = 16
+    _, _, full, cached = _layers(k3, cfg, 8, n_slots)
+    for bad in ([cfg.E], [-1], [0, cfg.E + 5]):
+        with pytest.raises(k3.K3MoEError) as ei:
+            cached.prefetch(bad)
+        assert ei.value.status == k3.K3MOE_EINVAL
+    cached.prefetch([])
+    x = _xd(synth.gen_x(cfg, T=2, stream=15))
+    _, idx, _ = cached.forward(x)
+    torch.cuda.synchronize()
+    used = set(idx.cpu().numpy().reshape(-1).tolist())
+    others = [e for e in range(cfg.E) if e not in used]
+    before = cached.stats()
+    with pytest.raises(k3.K3MoEError) as ei:
+        cached.prefetch(others[:n_slots - len(used) + 1])
+    assert ei.value.status == k3.K3MOE_EUNSUPPORTED
+    assert cached.stats() == before
+    cached.prefetch(others[:n_slots - len(used)])  # exactly the free slots
+    y0, _, _ = full.forward(x)
+    y1, _, _ = cached.forward(x)  # its experts are still resident
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    st = cached.stats()
+    assert st["misses"] == before["misses"] and st["prefetch_hits"] == 0
+    assert st["prefetched"] == n_slots - len(used)
+    cached.close()
+    full.close()
