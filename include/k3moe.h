@@ -230,8 +230,9 @@ int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int
  * waits on the host for the routing (one device-to-host copy of T*k indices)
  * before it enqueues the expert copies and kernels, so it returns once those
  * are enqueued, not when they finish. Calls on one cache must use one stream
- * (or be ordered by the caller). After a failed call the cache forgets every
- * resident expert (the next call copies what it needs again). */
+ * (or be ordered by the caller). A failed call waits for what it had
+ * enqueued on its stream, then forgets every resident expert (the next call
+ * copies what it needs again). */
 int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int32_t* topk_idx,
                         float* topk_gate, void* stream);
 
@@ -253,7 +254,8 @@ int k3moe_cache_stats(const k3moe_cache* c, int64_t* calls, int64_t* hits, int64
  * caller). Errors: K3MOE_EINVAL for a NULL cache, n < 0 or an id outside
  * [0, E); K3MOE_EUNSUPPORTED, with nothing changed, if more experts need a
  * slot than such slots exist; K3MOE_EHIP if a copy cannot be enqueued (the
- * cache then forgets every resident expert). */
+ * call then waits for the copies it had enqueued and the cache forgets every
+ * resident expert). */
 int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void* stream);
 
 /* Prefetch counters (HOST outputs, any may be NULL): experts copied in by

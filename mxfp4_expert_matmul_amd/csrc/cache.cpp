@@ -124,7 +124,12 @@ void place(k3moe_cache* c, int32_t e, int32_t v) {
   c->slot_of[(size_t)e] = v;
 }
 
-int fail(k3moe_cache* c, int rc) {
+// A failed forward or prefetch: wait for whatever it enqueued on st (so no
+// copy of it is still in flight when another stream reuses a slot), clear the
+// error and forget every resident expert.
+int fail(k3moe_cache* c, int rc, hipStream_t st) {
+  (void)hipStreamSynchronize(st);
+  (void)hipGetLastError();
   forget(c);
   return rc;
 }
@@ -266,11 +271,11 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
 
   // 1. route over all experts and read the selection back
   int rc = k3moe_route(c->route, x, T, nullptr, c->idx_dev, c->gate_dev, stream);
-  if (rc != K3MOE_OK) return fail(c, rc);
+  if (rc != K3MOE_OK) return fail(c, rc, st);
   if (hipMemcpyAsync(c->idx_host, c->idx_dev, P * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(c, K3MOE_EHIP);
+    return fail(c, K3MOE_EHIP, st);
   }
 
   // 2. the call's distinct experts; refuse before changing anything if they
@@ -289,7 +294,7 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
   if (c->pf_pending) {
     if (hipStreamWaitEvent(st, c->pf_ev, 0) != hipSuccess) {
       (void)hipGetLastError();
-      return fail(c, K3MOE_EHIP);
+      return fail(c, K3MOE_EHIP, st);
     }
     c->pf_pending = false;
   }
@@ -315,7 +320,7 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     place(c, e, v);
     if (copy_in(c, e, v, st) != hipSuccess) {
       (void)hipGetLastError();
-      return fail(c, K3MOE_EHIP);
+      return fail(c, K3MOE_EHIP, st);
     }
     c->last_use[(size_t)v] = call;
     ++misses;
@@ -335,17 +340,17 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
   }
   if (hipMemcpyAsync(c->sidx_dev, c->sidx_host, P * 4, hipMemcpyHostToDevice, st) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(c, K3MOE_EHIP);
+    return fail(c, K3MOE_EHIP, st);
   }
   // 5. the expert kernels over the arena
   rc = k3moe_experts_forward(c->arena, x, T, c->sidx_dev, c->gate_dev, y, stream);
-  if (rc != K3MOE_OK) return fail(c, rc);
+  if (rc != K3MOE_OK) return fail(c, rc, st);
   if ((topk_idx && hipMemcpyAsync(topk_idx, c->idx_dev, P * 4, hipMemcpyDeviceToDevice, st) !=
                        hipSuccess) ||
       (topk_gate && hipMemcpyAsync(topk_gate, c->gate_dev, P * 4, hipMemcpyDeviceToDevice, st) !=
                         hipSuccess)) {
     (void)hipGetLastError();
-    return fail(c, K3MOE_EHIP);
+    return fail(c, K3MOE_EHIP, st);
   }
   ++c->calls;
   c->hits += hits;
@@ -393,9 +398,8 @@ int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void
       if (eligible(s) && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v])) v = s;
     place(c, e, v);
     if (copy_in(c, e, v, st) != hipSuccess) {
-      (void)hipGetLastError();
       c->pf_pending = false;
-      return fail(c, K3MOE_EHIP);
+      return fail(c, K3MOE_EHIP, st);
     }
     c->last_use[(size_t)v] = pst;
     c->pre[(size_t)v] = 1;
@@ -403,7 +407,7 @@ int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void
   }
   if (hipEventRecord(c->pf_ev, st) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(c, K3MOE_EHIP);
+    return fail(c, K3MOE_EHIP, st);
   }
   c->pf_pending = true;
   c->prefetched += copied;
