@@ -370,23 +370,29 @@ int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void
   if (!guard.ok) return K3MOE_EHIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t pst = ++c->stamp;
-  // distinct listed experts; resident ones are refreshed, the rest need slots
+  // slots a prefetch may fill: not used by the last forward (its kernels may
+  // still run) and not taken (filled or refreshed) by this prefetch
+  auto eligible = [&](int32_t s) {
+    return (c->last_fwd == 0 || c->fwd_use[(size_t)s] != c->last_fwd) && c->last_use[(size_t)s] < pst;
+  };
+  // distinct listed experts: the resident ones in such slots are refreshed
+  // (which takes their slots), the ones not resident need a slot each;
+  // refuse before changing anything if too few slots are left for them
   c->uniq.clear();
+  int32_t refreshed = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t e = experts[i];
     if (c->seen[(size_t)e] == pst) continue;
     c->seen[(size_t)e] = pst;
-    if (c->slot_of[(size_t)e] < 0) c->uniq.push_back(e);
+    const int32_t s = c->slot_of[(size_t)e];
+    if (s < 0)
+      c->uniq.push_back(e);
+    else if (eligible(s))
+      ++refreshed;
   }
-  // slots a prefetch may fill: not used by the last forward (its kernels may
-  // still run) and not taken by this prefetch; refuse before changing anything
-  // if there are too few
-  auto eligible = [&](int32_t s) {
-    return (c->last_fwd == 0 || c->fwd_use[(size_t)s] != c->last_fwd) && c->last_use[(size_t)s] < pst;
-  };
   int32_t free_slots = 0;
   for (int32_t s = 0; s < c->n_slots; ++s) free_slots += eligible(s) ? 1 : 0;
-  if ((int32_t)c->uniq.size() > free_slots) return K3MOE_EUNSUPPORTED;
+  if ((int32_t)c->uniq.size() > free_slots - refreshed) return K3MOE_EUNSUPPORTED;
   for (int32_t i = 0; i < n; ++i) {  // refresh the resident ones
     const int32_t s = c->slot_of[(size_t)experts[i]];
     if (s >= 0 && eligible(s)) c->last_use[(size_t)s] = pst;
@@ -396,6 +402,10 @@ int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void
     int32_t v = -1;
     for (int32_t s = 0; s < c->n_slots; ++s)
       if (eligible(s) && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v])) v = s;
+    if (v < 0) {  // cannot happen after the count above; never index with it
+      c->pf_pending = false;
+      return fail(c, K3MOE_EUNSUPPORTED, st);
+    }
     place(c, e, v);
     if (copy_in(c, e, v, st) != hipSuccess) {
       c->pf_pending = false;

@@ -229,7 +229,7 @@ def test_prefetch_refusals(k3):
     needs more slots than those the last call leaves free is refused with
     nothing changed, and the cache keeps working."""
     cfg = synth.CONFIGS[1]
-    n_slots = 16
+    n_slots = 20  # a call of 2 tokens uses at most 16: at least 4 stay free
     _, _, full, cached = _layers(k3, cfg, 8, n_slots)
     for bad in ([cfg.E], [-1], [0, cfg.E + 5]):
         with pytest.raises(k3.K3MoEError) as ei:
@@ -246,13 +246,22 @@ def test_prefetch_refusals(k3):
         cached.prefetch(others[:n_slots - len(used) + 1])
     assert ei.value.status == k3.K3MOE_EUNSUPPORTED
     assert cached.stats() == before
-    cached.prefetch(others[:n_slots - len(used)])  # exactly the free slots
+    free = n_slots - len(used)
+    cached.prefetch(others[:free])  # exactly the free slots
+    # listed resident experts are refreshed, which takes their slots: the
+    # free ones refreshed leave no slot for one more expert
+    filled = cached.stats()
+    with pytest.raises(k3.K3MoEError) as ei:
+        cached.prefetch(others[:free] + [others[free]])
+    assert ei.value.status == k3.K3MOE_EUNSUPPORTED
+    assert cached.stats() == filled
+    cached.prefetch(others[1:free] + [others[free]])  # one slot left by the refresh
     y0, _, _ = full.forward(x)
     y1, _, _ = cached.forward(x)  # its experts are still resident
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     st = cached.stats()
     assert st["misses"] == before["misses"] and st["prefetch_hits"] == 0
-    assert st["prefetched"] == n_slots - len(used)
+    assert st["prefetched"] == free + 1
     cached.close()
     full.close()
