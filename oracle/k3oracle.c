@@ -30,7 +30,8 @@
  *     rounded to fp32; an optional fp32 bias is then added in fp32, before
  *     both selection and softmax;
  *   - top-k by (logit descending, expert index ascending); +0 and -0 are
- *     equal; a NaN logit ranks as -infinity;
+ *     equal; a NaN logit counts as -infinity, in the ranking (so it ties
+ *     with -inf and the lower index goes first) and in the gates (gate 0);
  *   - gates: softmax over the k selected logits in fp64 (the same as a full
  *     softmax renormalised over the selection);
  *   - expert: g = Wg x, u = Wu x, h = SiLU(g) * u with SiLU(z) = z/(1+e^-z),
@@ -151,12 +152,18 @@ int k3o_router_logits(const uint16_t *x, const float *wr, const float *bias,
     return K3O_OK;
 }
 
+/* A logit as the selection and the softmax see it: NaN is -infinity. */
+static double logit_value(float l)
+{
+    return isnan(l) ? -INFINITY : (double)l;
+}
+
 /* Order of the selection: a before b when l_a > l_b, or l_a == l_b and
  * a < b. A NaN logit compares as -infinity. */
 static int ranks_before(float la, int64_t a, float lb, int64_t b)
 {
-    double va = isnan(la) ? -INFINITY : (double)la;
-    double vb = isnan(lb) ? -INFINITY : (double)lb;
+    double va = logit_value(la);
+    double vb = logit_value(lb);
     if (va != vb)
         return va > vb;
     return a < b;
@@ -164,7 +171,10 @@ static int ranks_before(float la, int64_t a, float lb, int64_t b)
 
 /* Per token: the k experts that rank first (repeated selection of the best
  * expert not yet taken), and gate_j = exp(l_j - l_first) / sum over the k
- * selected of exp(l - l_first), in fp64. idx [T][k] int32, gate [T][k]. */
+ * selected of exp(l - l_first), in fp64. A selected NaN logit counts as
+ * -infinity here too, so its gate is 0 (when every selected logit is -inf or
+ * NaN, l_j - l_first is NaN and so are all the gates). idx [T][k] int32,
+ * gate [T][k]. */
 int k3o_topk_gates(const float *logits, int64_t T, int64_t E, int64_t k,
                    int32_t *idx, double *gate)
 {
@@ -187,10 +197,10 @@ int k3o_topk_gates(const float *logits, int64_t T, int64_t E, int64_t k,
             }
             sel[j] = (int32_t)best;
         }
-        double l0 = (double)row[sel[0]];
+        double l0 = logit_value(row[sel[0]]);
         double sum = 0.0;
         for (int64_t j = 0; j < k; ++j) {
-            gate[t * k + j] = exp((double)row[sel[j]] - l0);
+            gate[t * k + j] = exp(logit_value(row[sel[j]]) - l0);
             sum += gate[t * k + j];
         }
         for (int64_t j = 0; j < k; ++j)

@@ -145,6 +145,50 @@ def test_topk_special_cases():
         assert list(idx[t]) == list(np.lexsort((np.arange(E), -row[t])))
 
 
+def test_topk_nan_logits_count_as_minus_inf():
+    """A NaN logit counts as -inf, in the ranking and in the gates. Pinned by
+    a chain of reductions to the brute force above: NaN -> -inf leaves
+    selection and gates unchanged; -inf -> one common finite value below
+    every other logit leaves the selection unchanged (equal values rank by
+    index), so the brute force over subsets decides it; the gates of the
+    selected -inf logits are exactly 0 and the others are the softmax of the
+    selected finite logits."""
+    # worked example: three finite logits, then the -inf/NaN ties by index
+    row = np.array([np.nan, 0.5, np.nan, -np.inf, 0.1, np.nan, -np.inf, 0.3], np.float32)
+    idx, gate = oracle.topk_gates(row[None, :], 5)
+    assert list(idx[0]) == [1, 7, 4, 0, 2]
+    assert np.allclose(gate[0, :3], softmax(np.array([0.5, 0.3, 0.1], np.float32).astype(np.float64)),
+                       rtol=1e-14, atol=0)
+    assert np.all(gate[0, 3:] == 0.0)
+    rng = np.random.default_rng(17)
+    E = 8
+    for trial in range(200):
+        k = int(rng.integers(1, E + 1))
+        row = (rng.integers(-2, 3, E) if trial % 2 else rng.standard_normal(E)).astype(np.float32)
+        kind = rng.integers(0, 3, E)  # 0 finite, 1 NaN, 2 -inf
+        kind[rng.integers(0, E)] = 0  # at least one finite logit
+        row[kind == 1] = np.nan
+        row[kind == 2] = -np.inf
+        idx, gate = oracle.topk_gates(row[None, :], k)
+        inf_row = np.where(np.isnan(row), np.float32(-np.inf), row)
+        idx2, gate2 = oracle.topk_gates(inf_row[None, :], k)
+        assert np.array_equal(idx, idx2) and np.array_equal(gate, gate2), (row, k)
+        fin = np.isfinite(inf_row)
+        low = np.float32(np.min(inf_row[fin]) - 64.0)
+        fin_row = np.where(fin, inf_row, low)
+        idx3, _ = oracle.topk_gates(fin_row[None, :], k)
+        assert np.array_equal(idx, idx3), (row, k)
+        assert list(idx3[0]) == _brute_topk(fin_row, k), (row, k)
+        sel = idx[0]
+        on = fin[sel]
+        assert np.all(gate[0][~on] == 0.0)
+        want = softmax(inf_row[sel[on]].astype(np.float64))
+        assert np.allclose(gate[0][on], want, rtol=1e-14, atol=0), (row, k)
+    # nothing finite: every gate is NaN (l_j - l_first is -inf - -inf)
+    idx, gate = oracle.topk_gates(np.array([[np.nan, -np.inf, np.nan]], np.float32), 2)
+    assert list(idx[0]) == [0, 1] and np.all(np.isnan(gate))
+
+
 def test_gates_sum_to_one_and_bias_selects():
     cfg = synth.CONFIGS[1]
     E, k = cfg.E, cfg.k
@@ -216,6 +260,36 @@ def test_zero_weights_give_zero():
         x = synth.gen_x(cfg, T=2)
         r = oracle.layer_forward(x, synth.gen_router_w(cfg), None, synth.ExpertSource(cfg, Z), cfg.k)
         assert np.all(r["y64"] == 0.0)
+
+
+def test_nan_scale_byte_propagates():
+    """E8M0 byte 0xFF is NaN (OCP MX v1.0): a NaN block in row m of an
+    expert's down projection makes exactly output m of the tokens routed to
+    that expert NaN; a NaN block in its gate projection makes every output of
+    those tokens NaN (through h). Tokens routed elsewhere stay finite and
+    equal to the unmodified layer."""
+    cfg = synth.CONFIGS[0]
+    W = synth.gen_weights(cfg)
+    wr = synth.gen_router_w(cfg)
+    x = synth.gen_x(cfg, T=12, stream=3)
+    base = oracle.layer_forward(x, wr, None, synth.ExpertSource(cfg, W), cfg.k)
+    used = np.unique(base["idx"])
+    e_down, e_gate = int(used[0]), int(used[1])
+    m0 = 5
+    W2 = {n: a.copy() for n, a in W.items()}
+    W2["down_s"][e_down, m0, 3] = 0xFF
+    W2["gate_s"][e_gate, 7, 2] = 0xFF
+    r = oracle.layer_forward(x, wr, None, synth.ExpertSource(cfg, W2), cfg.k)
+    assert np.array_equal(r["idx"], base["idx"])
+    for t in range(x.shape[0]):
+        sel = set(r["idx"][t].tolist())
+        want = np.zeros(cfg.d, dtype=bool)
+        if e_down in sel:
+            want[m0] = True
+        if e_gate in sel:
+            want[:] = True
+        assert np.array_equal(np.isnan(r["y64"][t]), want), t
+        assert np.array_equal(r["y64"][t][~want], base["y64"][t][~want]), t
 
 
 def test_scale_homogeneity():
