@@ -37,8 +37,15 @@
  * - A handle owns one workspace; calls on one handle must not overlap (use one
  *   handle per concurrent stream).
  * - T = 0 is valid and does nothing.
- * - NaN/Inf inputs propagate and are not checked; a NaN router logit never
- *   wins a selection (it ranks as -inf), so selected indices stay in range.
+ * - NaN/Inf inputs are not checked and propagate, except in the router: a
+ *   NaN logit counts as -inf. In the selection it ranks equal to -inf (ties
+ *   to the lower index), so it is chosen only when fewer than k logits lie
+ *   above -inf; in the gates a selected one gets gate 0. Selected indices
+ *   therefore always lie in [0, E).
+ * - An E8M0 scale byte 0xFF is NaN and propagates through the sums it
+ *   enters: a NaN block in row m of an expert's down projection makes
+ *   output m of the tokens routed to that expert NaN; one in its gate or up
+ *   projection makes all outputs of those tokens NaN.
  */
 #ifndef K3MOE_H
 #define K3MOE_H

@@ -159,7 +159,8 @@ def test_cache_create_rejects_bad_arguments(k3):
 def test_cached_k3_decode_equals_resident(k3):
     """K3 shape (896 experts, 21 GB of MXFP4 experts in pinned host memory)
     behind a 64-slot arena: decode steps that miss and evict give exactly the
-    resident layer's outputs."""
+    resident layer's outputs, with and without a prefetch of the next step
+    overlapping the current one."""
     from synth.device import device_weights, device_x
     cfg = synth.CONFIGS[2]
     dw = device_weights(cfg, torch.device("cuda:0"))
@@ -173,7 +174,7 @@ def test_cached_k3_decode_equals_resident(k3):
     c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, 1)
     full = k3.Layer(c, dw, 0)
     cached = k3.CachedLayer(c, host, 64, 0)
-    xp = device_x(cfg, T=8, stream=10, device=torch.device("cuda:0"))
+    xp = device_x(cfg, T=16, stream=10, device=torch.device("cuda:0"))
     for i in range(8):
         y0, i0, _ = full.forward(xp[i:i + 1])
         y1, i1, _ = cached.forward(xp[i:i + 1])
@@ -181,45 +182,60 @@ def test_cached_k3_decode_equals_resident(k3):
         assert torch.equal(i0, i1) and torch.equal(y0, y1), f"token {i}"
     st = cached.stats()
     assert st["calls"] == 8 and st["misses"] >= 64  # the arena was refilled
+    # then 8 more decode steps, each prefetched on a copy stream while the
+    # previous step's expert kernels run
+    xs = [xp[i:i + 1] for i in range(8, 16)]
+    refs = [full.forward(x) for x in xs]
+    torch.cuda.synchronize()
+    st, new = _prefetch_overlapped(cached, xs, refs, cfg)
+    assert new > 0
     cached.close()
     full.close()
     del dw, host
     torch.cuda.empty_cache()
 
 
+def _prefetch_overlapped(cached, xs, refs, cfg):
+    """Call n + 1's experts are prefetched on a copy stream right after call n
+    is enqueued, while call n's expert kernels may still run (its kernels read
+    the slots the prefetch must not overwrite); no synchronisation until the
+    last call. Every output must equal the resident layer's bit for bit.
+    After the first call nothing is missed, every prefetched expert is a
+    prefetch hit, and raw hits (all) exceed true resident hits (hits minus
+    prefetch hits) by exactly those."""
+    lists = [r[1].cpu().numpy().reshape(-1).tolist() for r in refs]  # host, before the calls
+    copy = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    start = cached.stats()
+    outs = [cached.forward(xs[0])]
+    after_first = cached.stats()
+    for n in range(1, len(xs)):
+        cached.prefetch(lists[n], stream=copy)
+        outs.append(cached.forward(xs[n]))
+    torch.cuda.synchronize()
+    for n, ((y, idx, gate), (ry, ri, rg)) in enumerate(zip(outs, refs)):
+        assert torch.equal(idx, ri) and torch.equal(gate, rg), f"call {n}: routing differs"
+        assert torch.equal(y, ry), f"call {n}: output differs"
+    st = cached.stats()
+    assert st["misses"] == after_first["misses"], "a prefetched expert was missed"
+    assert st["hits"] - after_first["hits"] == sum(len(set(li)) for li in lists[1:])
+    new = st["prefetched"] - start["prefetched"]
+    assert st["prefetch_hits"] - start["prefetch_hits"] == new
+    assert st["bytes_in"] - after_first["bytes_in"] == new * cfg.expert_bytes()
+    return st, new
+
+
 def test_prefetch_ahead_on_a_copy_stream(k3):
-    """Each call's experts are prefetched on a second stream right after the
-    previous call is enqueued (its kernels may still run). Outputs equal the
-    resident layer bit for bit. After the first call nothing is missed, every
-    prefetched expert is a prefetch hit, and raw hits (all) exceed true
-    resident hits (hits minus prefetch hits) by exactly those."""
-    cfg = synth.CONFIGS[1]  # 64 experts, top-8
+    """Small shape (64 experts, top-8, 40 slots), 12 calls of 2 tokens."""
+    cfg = synth.CONFIGS[1]
     T, n_calls = 2, 12
     _, _, full, cached = _layers(k3, cfg, 8, 40)
     pool = synth.gen_x(cfg, T=T * n_calls, stream=14)
     xs = [_xd(pool[i * T:(i + 1) * T]) for i in range(n_calls)]
-    refs = [full.forward(x) for x in xs]  # reference outputs and each call's routing
+    refs = [full.forward(x) for x in xs]
     torch.cuda.synchronize()
-    copy = torch.cuda.Stream()
-    y, idx, _ = cached.forward(xs[0])
-    torch.cuda.synchronize()
-    assert torch.equal(y, refs[0][0]) and torch.equal(idx, refs[0][1])
-    prev = cached.stats()
-    for n in range(1, n_calls):
-        experts = refs[n][1].cpu().numpy().reshape(-1).tolist()
-        cached.prefetch(experts, stream=copy)
-        y, idx, gate = cached.forward(xs[n])
-        torch.cuda.synchronize()
-        assert torch.equal(idx, refs[n][1]) and torch.equal(gate, refs[n][2]), f"call {n}"
-        assert torch.equal(y, refs[n][0]), f"call {n}: output differs"
-        st = cached.stats()
-        new = st["prefetched"] - prev["prefetched"]
-        assert st["misses"] == prev["misses"], f"call {n}: a prefetched expert was missed"
-        assert st["hits"] - prev["hits"] == len(set(experts))
-        assert st["prefetch_hits"] - prev["prefetch_hits"] == new
-        assert st["bytes_in"] - prev["bytes_in"] == new * cfg.expert_bytes()
-        prev = st
-    assert prev["prefetched"] > 0 and prev["hits"] - prev["prefetch_hits"] > 0
+    st, new = _prefetch_overlapped(cached, xs, refs, cfg)
+    assert new > 0 and st["hits"] - st["prefetch_hits"] > 0
     cached.close()
     full.close()
 

@@ -29,6 +29,7 @@ def k3():
 
 
 GATE_TOL = 4e-5
+TILE_M = 96  # tokens per tile of the grouped expert GEMM (kTileM in the kernels)
 
 
 def _say(msg):
@@ -84,6 +85,12 @@ def _run_and_check(k3, layer, cfg, x_bits, src, wr, bias, tokens=None, label="")
     yref = oracle.experts_forward(x_bits[check], use_idx, use_gate, src)
     ratio = check_output(y[check], yref, label)
     _say(f"[{label}] T={T} checked {len(check)} tokens, max|err|/rms = {ratio:.3e}, excused {len(excused)}")
+    if len(check) > 1:
+        rms = float(np.sqrt(np.mean(yref ** 2)))
+        per = np.max(np.abs(y[check].astype(np.float64) - yref), axis=1) / rms
+        worst = np.argsort(-per)[:8]
+        _say(f"[{label}] worst tokens (token: max|err|/rms): "
+             + ", ".join(f"{int(check[i])}: {per[i]:.2e}" for i in worst))
     return y, idx, gate
 
 
@@ -216,6 +223,110 @@ def test_activation_outlier_channels(k3, T):
     xf[:, ch] *= 32.0  # exact in bf16
     x = synth.f32_to_bf16_bits(xf)
     _run_and_check(k3, layer, cfg, x, s.src, s.wr, s.bias, label=f"outlier channels T={T}")
+    layer.close()
+
+
+class Biased(Small):
+    """A small layer with the seeded weights and a caller-chosen router bias."""
+
+    def __init__(self, cfg, bias):
+        import mxfp4_expert_matmul_amd as k3m
+        from synth.device import host_weights_to_device
+        self.cfg = cfg
+        self.W = synth.gen_weights(cfg)
+        self.wr = synth.gen_router_w(cfg)
+        self.bias = np.asarray(bias, dtype=np.float32)
+        self.src = synth.ExpertSource(cfg, self.W)
+        self.dw = k3m.pack_layer_weights(host_weights_to_device(self.W, self.wr, self.bias),
+                                         cfg.E, cfg.d, cfg.f)
+
+
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_nan_router_bias_never_selected(k3, T):
+    """NaN bias entries make those experts' logits NaN for every token; a NaN
+    logit ranks as -inf, so with enough finite logits it is never selected,
+    and routing, gates and outputs match the oracle (the top-k fused into the
+    decode GEMV for T <= 4, the top-k kernel above). The NaN experts are the
+    ones the bias would otherwise rank first."""
+    cfg = synth.CONFIGS[1]
+    bias = 0.5 * np.random.default_rng(61).standard_normal(cfg.E).astype(np.float32)
+    nan_experts = np.concatenate([np.argsort(-bias)[:3], [0, 17, cfg.E - 1]])
+    bias[nan_experts] = np.nan
+    s = Biased(cfg, bias)
+    layer = _layer(k3, cfg, s.dw, max(T, 8))
+    x = synth.gen_x(cfg, T=T, stream=16)
+    _, idx, _ = _run_and_check(k3, layer, cfg, x, s.src, s.wr, s.bias, label=f"NaN bias T={T}")
+    assert not np.any(np.isin(idx, nan_experts)), "a NaN-logit expert was selected"
+    layer.close()
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_nan_router_bias_fewer_than_k_finite(k3, T):
+    """Only one finite logit per token with k = 2: the second selection is the
+    lowest-index NaN expert (NaN ties with -inf, lower index first) with gate
+    exactly 0, and the output is the finite expert's alone."""
+    cfg = EDGE
+    bias = np.full(cfg.E, np.nan, dtype=np.float32)
+    bias[5] = 0.25
+    s = Biased(cfg, bias)
+    layer = _layer(k3, cfg, s.dw, 8)
+    x = synth.gen_x(cfg, T=T, stream=17)
+    _, idx, gate = _run_and_check(k3, layer, cfg, x, s.src, s.wr, s.bias,
+                                  label=f"one finite logit T={T}")
+    assert np.all(idx == np.array([5, 0], dtype=np.int32))
+    assert np.all(gate[:, 0] == 1.0) and np.all(gate[:, 1] == 0.0)
+    layer.close()
+
+
+def _check_with_nans(y_gpu, y_ref, label):
+    """NaN positions must match exactly; finite outputs meet the parity bar
+    against the RMS of the finite reference outputs."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    nan_g, nan_r = np.isnan(y_gpu), np.isnan(y_ref)
+    assert np.array_equal(nan_g, nan_r), (f"{label}: NaN at {int(nan_g.sum())} outputs, "
+                                          f"expected {int(nan_r.sum())}")
+    fin = ~nan_r
+    assert np.any(fin), f"{label}: no finite output to compare"
+    assert np.all(np.isfinite(y_gpu[fin])), f"{label}: Inf where the reference is finite"
+    rms = float(np.sqrt(np.mean(y_ref[fin] ** 2)))
+    err = float(np.max(np.abs(y_gpu[fin] - y_ref[fin])))
+    assert err <= 2e-2 * rms, f"{label}: max abs err {err:.4g} > 2e-2 * rms {rms:.4g}"
+    return int(nan_r.sum()), err / rms
+
+
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_nan_scale_block_propagates(k3, T):
+    """An E8M0 scale byte 0xFF (NaN) in one block: in row m of an expert's
+    down projection it makes output m of the tokens routed there NaN and
+    nothing else; in a row of another expert's gate projection, and of a
+    third expert's up projection, it makes every output of their tokens NaN
+    (through h). The NaN pattern equals the oracle's exactly, on the decode
+    GEMV (T <= 4) and the grouped MFMA GEMM (T > 4)."""
+    cfg = EDGE
+    x = synth.gen_x(cfg, T=T, stream=18)
+    wr = synth.gen_router_w(cfg)
+    ridx, _ = oracle.topk_gates(oracle.router_logits(x, wr, None), cfg.k)
+    used = list(dict.fromkeys(int(e) for e in ridx.reshape(-1)))
+    W = synth.gen_weights(cfg)
+    m0 = 37
+    W["down_s"][used[0], m0, 3] = 0xFF  # token 0's first expert: its output m0 only
+    # gate and up blocks on experts token 0 does not use, so its other
+    # outputs stay finite
+    others = [e for e in used if e not in ridx[0]]
+    if len(others) > 0:
+        W["gate_s"][others[0], 7, 2] = 0xFF
+    if len(others) > 1:
+        W["up_s"][others[1], 100, 5] = 0xFF
+    s = Custom(cfg, W)
+    layer = _layer(k3, cfg, s.dw, 64)
+    y, idx, _ = layer.forward(_x_dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    yref = oracle.experts_forward(x, ridx, oracle.topk_gates(oracle.router_logits(x, wr, None), cfg.k)[1],
+                                  s.src)
+    n_nan, ratio = _check_with_nans(y.cpu().numpy(), yref, f"NaN scale T={T}")
+    assert n_nan > 0
+    _say(f"[NaN scale T={T}] {n_nan} NaN outputs as expected; finite max|err|/rms = {ratio:.3e}")
     layer.close()
 
 
@@ -444,6 +555,48 @@ def test_abi_rejects_bad_calls(k3):
     layer.close()
 
 
+def _sample_tokens(ridx, E, n, seed, label):
+    """Seeded sample of n tokens whose outputs are checked, chosen so the
+    grouped GEMM's hard places are in it. Pairs are grouped by (expert, token)
+    and cut into tiles of TILE_M consecutive tokens of one expert, so an
+    expert's i-th token (in token order) sits in row i % TILE_M of tile
+    i // TILE_M. The sample always holds: the first and last token; the
+    hottest expert's first tile (rows 0, 1, 17, 40, the last) and last tile
+    (its first row, a row past 16 when the tile has one, its last row); the
+    first and last rows of the last partial tile of the next hottest experts
+    with more than TILE_M tokens; a row past 16 of an expert with 17..TILE_M
+    tokens. The rest are seeded random tokens."""
+    T = ridx.shape[0]
+    counts = np.bincount(ridx.reshape(-1), minlength=E)
+    order = np.argsort(-counts, kind="stable")
+    per = lambda e: np.nonzero(np.any(ridx == e, axis=1))[0]  # noqa: E731
+    want = [0, T - 1]
+    hot = int(order[0])
+    ht = per(hot)
+    c = len(ht)
+    last0 = TILE_M * ((c - 1) // TILE_M)
+    for i in (0, 1, 17, 40, min(TILE_M, c) - 1, last0, last0 + 20, c - 1):
+        if 0 <= i < c and (i < TILE_M or i >= last0):
+            want.append(int(ht[i]))
+    multi = [int(e) for e in order[1:] if counts[e] > TILE_M][:3]
+    for e in multi:
+        et = per(e)
+        l0 = TILE_M * ((len(et) - 1) // TILE_M)
+        want += [int(et[l0]), int(et[-1])]
+    mid = [int(e) for e in order if 16 < counts[e] <= TILE_M]
+    if mid:
+        et = per(mid[0])
+        want += [int(et[16]), int(et[-1])]
+    want = list(dict.fromkeys(want))[:n]
+    rng = np.random.default_rng(seed)
+    rest = rng.permutation(np.setdiff1d(np.arange(T), want))[:max(0, n - len(want))]
+    tokens = np.sort(np.concatenate([np.asarray(want, dtype=np.int64), rest]))
+    _say(f"[{label}] hottest expert {hot}: {c} tokens ({(c + TILE_M - 1) // TILE_M} tiles); "
+         f"experts touched {int((counts > 0).sum())}; experts over one tile {int((counts > TILE_M).sum())}; "
+         f"checking {len(tokens)} tokens, {len(want)} chosen for their tile rows")
+    return tokens
+
+
 # ----------------------------------------------------------------- K3 scale
 
 @pytest.fixture(scope="module")
@@ -508,8 +661,9 @@ def test_k3_prefill_256(k3, big_layers):
     st = big_layers(3, 4096)
     cfg = st["cfg"]
     x = synth.gen_x(cfg)
-    rng = np.random.default_rng(cfg.seed)
-    tokens = np.sort(np.concatenate([[0, cfg.T - 1], rng.choice(np.arange(1, cfg.T - 1), 2, replace=False)]))
+    logits = oracle.router_logits(x, st["wr"], st["bias"])
+    ridx, _ = oracle.topk_gates(logits, cfg.k)
+    tokens = _sample_tokens(ridx, cfg.E, 64, cfg.seed, "k3 prefill 256")
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
                    label="k3 prefill 256")
 
@@ -520,15 +674,9 @@ def test_k3_prefill_4096_skewed(k3, big_layers):
     st = big_layers(4, 4096)
     cfg = st["cfg"]
     x = synth.gen_x(cfg)
-    # tokens routed to the hottest expert are in the sample
     logits = oracle.router_logits(x, st["wr"], st["bias"])
     ridx, _ = oracle.topk_gates(logits, cfg.k)
-    counts = np.bincount(ridx.reshape(-1), minlength=cfg.E)
-    hot = int(np.argmax(counts))
-    _say(f"hottest expert {hot} with {counts[hot]} tokens; experts touched {int((counts > 0).sum())}")
-    hot_tokens = np.nonzero(np.any(ridx == hot, axis=1))[0]
-    rng = np.random.default_rng(cfg.seed)
-    tokens = np.unique(np.concatenate([hot_tokens[:2], [cfg.T - 1], rng.choice(cfg.T, 1)]))
+    tokens = _sample_tokens(ridx, cfg.E, 64, cfg.seed, "k3 prefill 4096 skew")
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
                    label="k3 prefill 4096 skew")
 
@@ -537,8 +685,9 @@ def test_k3_prefill_4096_skewed(k3, big_layers):
 def test_k3_prefill_max_tokens(k3, big_layers):
     """The largest T the K3 shape accepts (T*k*f = 2^30: 32768 tokens, 524288
     pairs): every offset of the grouped path at its widest. Routing is checked
-    for every token, outputs for tokens of the hottest expert, the first and
-    the last token."""
+    for every token, outputs for 16 sampled tokens that include the hottest
+    expert's first and last tiles, rows past 16 inside a tile and another
+    expert's last partial tile."""
     st = big_layers(4, 4096)
     cfg = st["cfg"]
     T = (1 << 30) // (cfg.k * cfg.f)
@@ -548,11 +697,7 @@ def test_k3_prefill_max_tokens(k3, big_layers):
     logits = oracle.router_logits(x, st["wr"], st["bias"])
     ridx, _ = oracle.topk_gates(logits, cfg.k)
     del logits
-    counts = np.bincount(ridx.reshape(-1), minlength=cfg.E)
-    hot = int(np.argmax(counts))
-    _say(f"hottest expert {hot} with {counts[hot]} tokens")
-    hot_tokens = np.nonzero(np.any(ridx == hot, axis=1))[0]
-    tokens = np.unique(np.concatenate([[0, T - 1], hot_tokens[[0, -1]]]))
+    tokens = _sample_tokens(ridx, cfg.E, 16, cfg.seed, f"k3 prefill T={T}")
     try:
         _run_and_check(k3, layer, cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
                        label=f"k3 prefill T={T}")
