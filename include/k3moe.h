@@ -149,6 +149,30 @@ int64_t k3moe_workspace_bytes(const k3moe_config* cfg);
 int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y,
                         int32_t* topk_idx, float* topk_gate, void* stream);
 
+/* The whole layer for decode-sized calls, with no handle and no allocation:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). It runs the
+ * same kernels as k3moe_layer_forward does for T <= 4 (router, gate/up with
+ * the top-k fused, down with the combine fused), on the CURRENT HIP device,
+ * and keeps its scratch (router logits, SwiGLU output h, and the routing when
+ * topk_idx/topk_gate are NULL) in a fixed 2 MiB device array that the library
+ * holds on each device for the life of the process. It calls no allocating
+ * routine. Every call on one device shares that array: calls that overlap on
+ * one device (two streams, or two host threads) race and must be ordered by
+ * the caller. The first call on a device takes the array's address and sets
+ * the kernels' LDS limits there.
+ *   cfg, w     as for k3moe_create (HOST structs; w holds DEVICE pointers on
+ *              the current device); cfg->max_tokens bounds T as usual
+ *   x, T, y    as for k3moe_layer_forward, 0 <= T <= 4
+ *   topk_idx, topk_gate  [T][k] outputs, both given or both NULL
+ * Returns K3MOE_EINVAL for malformed arguments, K3MOE_EUNSUPPORTED when T > 4
+ * or the scratch needed, 256-byte aligned slices of T*E*4 bytes of logits,
+ * T*k*f*4 of h and (routing not given) 2*T*k*4 of idx/gate, exceeds 2 MiB
+ * (the K3 shape d=7168, E=896, k=16, f=2048 needs 0.54 MB at T = 4). */
+int k3moe_layer_forward_noalloc(const k3moe_config* cfg, const k3moe_weights* w,
+                                const void* x, int32_t T, float* y,
+                                int32_t* topk_idx, float* topk_gate, void* stream);
+
 /* Router step alone: fp32 logits, top-k selection with ties to the lower
  * index, and gates renormalised over the selection.
  *   logits [T][E] fp32 output, or NULL to skip writing them

@@ -104,6 +104,9 @@ def load_library():
     lib.k3moe_cache_destroy.restype = None
     lib.k3moe_cache_prefetch.argtypes = [vp, vp, i32, vp]
     lib.k3moe_cache_prefetch.restype = ctypes.c_int
+    lib.k3moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights),
+                                                vp, i32, vp, vp, vp, vp]
+    lib.k3moe_layer_forward_noalloc.restype = ctypes.c_int
     lib.k3moe_cache_prefetch_stats.argtypes = [vp, vp, vp]
     lib.k3moe_cache_prefetch_stats.restype = ctypes.c_int
     _lib = lib
@@ -158,6 +161,19 @@ def k3moe_layer_forward(handle, x, y, topk_idx=None, topk_gate=None, stream=None
     rc = load_library().k3moe_layer_forward(handle, _ptr(x), T, _ptr(y), _ptr(topk_idx),
                                             _ptr(topk_gate), _stream(stream, device or x.device))
     _check(rc, "k3moe_layer_forward")
+
+
+def k3moe_layer_forward_noalloc(cfg: Config, weights: dict, x, y, topk_idx=None, topk_gate=None,
+                                stream=None):
+    """Decode-sized forward (T <= 4) without a handle or any allocation, on
+    the current device; weights as for k3moe_create."""
+    c = cfg._c()
+    w = _Weights(*[weights.get(n).data_ptr() if weights.get(n) is not None else None
+                   for n, _ in _Weights._fields_])
+    rc = load_library().k3moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), _ptr(x),
+                                                    x.shape[0], _ptr(y), _ptr(topk_idx),
+                                                    _ptr(topk_gate), _stream(stream, x.device))
+    _check(rc, "k3moe_layer_forward_noalloc")
 
 
 def k3moe_route(handle, x, idx, gate, logits=None, stream=None):

@@ -462,6 +462,29 @@ hipError_t prepare_gemv(const Shape& s) {
   }
 }
 
+// Every decode kernel instantiation's dynamic LDS limit. Each limit is fixed by
+// the instantiation's template arguments, so this does not depend on a shape.
+hipError_t prepare_gemv_all() {
+  hipError_t e = hipSuccess;
+  auto gu = [&](const void* fn, int xc) {
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 1024 * xc);
+  };
+#define K3_GU_ALL(XC)                                                       \
+  gu(reinterpret_cast<const void*>(gemv_gateup_kernel<XC, 16>), XC);        \
+  gu(reinterpret_cast<const void*>(gemv_gateup_kernel<XC, 64>), XC)
+  K3_GU_ALL(2);
+  K3_GU_ALL(4);
+  K3_GU_ALL(8);
+  K3_GU_ALL(14);
+  K3_GU_ALL(16);
+#undef K3_GU_ALL
+  if (e == hipSuccess) e = set_down_lds_nc<1>();
+  if (e == hipSuccess) e = set_down_lds_nc<2>();
+  if (e == hipSuccess) e = set_down_lds_nc<4>();
+  return e;
+}
+
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st) {
   if (T <= 0) return hipSuccess;

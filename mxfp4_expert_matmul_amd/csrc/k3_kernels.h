@@ -55,8 +55,10 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const Ex
                               hipStream_t st);
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st);
-// once per handle: raise the dynamic LDS limit the decode down kernel needs
+// once per handle: raise the dynamic LDS limits the decode kernels of shape s need
 hipError_t prepare_gemv(const Shape& s);
+// the same for every decode kernel instantiation (no shape needed)
+hipError_t prepare_gemv_all();
 
 // gemm.hip (prefill path)
 hipError_t launch_quant_x(const uint16_t* x, int T, int d, uint8_t* xq, uint8_t* xs,

@@ -7,6 +7,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -246,6 +247,48 @@ int check_tokens(const k3moe* h, int32_t T) {
   return K3MOE_OK;
 }
 
+// ------------------------------------------------------ no-allocation decode
+// k3moe_layer_forward_noalloc serves callers that cannot allocate (code under
+// HIP graph capture, serving loops, harnesses that forbid hipMalloc). It runs
+// the decode path (T <= kGemvMaxT: router GEMV, gate/up GEMV with the top-k
+// fused, down GEMV with the combine fused) with its scratch -- the logits,
+// the routing when the caller passes none, and the SwiGLU output h -- in this
+// file-scope device array. Each device holds its own copy for the life of
+// the process; calls on one device share it (overlapping calls race).
+constexpr size_t kScratchBytes = (size_t)2 << 20;  // 2 MiB
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The array's device address, taken once per device with that device
+// current (host code never passes the array's own name to a kernel: on the
+// host it names a stand-in, not device memory).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_of_device(int dev, uint8_t** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    // the decode kernels' dynamic LDS limits, once per device
+    e = k3::prepare_gemv_all();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+
+// Scratch bytes a decode call of T tokens needs (logits, h, and idx/gate
+// when the caller passes none), each slice 256-byte aligned.
+size_t noalloc_scratch_bytes(const k3moe_config* c, int T, bool own_routing) {
+  const size_t P = (size_t)T * c->top_k;
+  size_t n = align_up((size_t)T * c->n_experts * 4) + align_up(P * c->d_ff * 4);
+  if (own_routing) n += 2 * align_up(P * 4);
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +490,56 @@ int k3moe_layer_forward(k3moe* h, const void* x, int32_t T, float* y, int32_t* t
     return rc2;
   }
   return run_experts(h, xb, T, idx, gate, y, st, fused_topk ? h->logits : nullptr, !fused_topk);
+}
+
+int k3moe_layer_forward_noalloc(const k3moe_config* cfg, const k3moe_weights* w, const void* x,
+                                int32_t T, float* y, int32_t* topk_idx, float* topk_gate,
+                                void* stream) {
+  int rc = check_config(cfg);
+  if (rc != K3MOE_OK) return rc;
+  if (!w) return K3MOE_EINVAL;
+  const void* req[] = {w->router_w, w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const void* p : req)
+    if (!p || !aligned(p, 16)) return K3MOE_EINVAL;
+  if (w->router_b && !aligned(w->router_b, 16)) return K3MOE_EINVAL;
+  if (T < 0 || T > cfg->max_tokens) return K3MOE_EINVAL;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return K3MOE_EINVAL;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_gate && !aligned(topk_gate, 4)))
+    return K3MOE_EINVAL;
+  if ((topk_idx == nullptr) != (topk_gate == nullptr)) return K3MOE_EINVAL;
+  // the decode path only, within the fixed scratch
+  if (T > k3::kGemvMaxT) return K3MOE_EUNSUPPORTED;
+  const bool own = topk_idx == nullptr;
+  if (noalloc_scratch_bytes(cfg, T, own) > kScratchBytes) return K3MOE_EUNSUPPORTED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return K3MOE_EHIP;
+  if (dev >= kMaxDevices) return K3MOE_EUNSUPPORTED;
+  uint8_t* base = nullptr;
+  if (scratch_of_device(dev, &base) != hipSuccess) {
+    (void)hipGetLastError();
+    return K3MOE_EHIP;
+  }
+  const size_t P = (size_t)T * cfg->top_k;
+  float* logits = reinterpret_cast<float*>(base);
+  size_t o = align_up((size_t)T * cfg->n_experts * 4);
+  float* h32 = reinterpret_cast<float*>(base + o);
+  o += align_up(P * cfg->d_ff * 4);
+  int32_t* idx = topk_idx;
+  float* gate = topk_gate;
+  if (own) {
+    idx = reinterpret_cast<int32_t*>(base + o);
+    o += align_up(P * 4);
+    gate = reinterpret_cast<float*>(base + o);
+  }
+  const Shape s{cfg->d_model, cfg->n_experts, cfg->top_k, cfg->d_ff};
+  const k3::ExpertWeights ew{w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  hipError_t e = k3::launch_router_logits(xb, T, s, w->router_w, nullptr, w->router_b, logits, st);
+  if (e == hipSuccess) e = k3::launch_gemv_gateup(xb, T, s, ew, logits, idx, gate, h32, st);
+  if (e == hipSuccess) e = k3::launch_gemv_down(T, s, ew, idx, gate, h32, y, st);
+  return hip_status(e);
 }
 
 

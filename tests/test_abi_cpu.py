@@ -97,3 +97,28 @@ def test_cache_create_validates_before_any_device_call(lib):
     assert out.value is None
     assert dll.k3moe_cache_stats(None, None, None, None, None) == lib.K3MOE_EINVAL
     dll.k3moe_cache_destroy(None)  # NULL-safe
+
+
+def test_noalloc_validates_before_any_device_call(lib):
+    """k3moe_layer_forward_noalloc checks its arguments on the host first:
+    malformed calls return EINVAL and calls beyond its scratch array or the
+    decode path return EUNSUPPORTED, without touching a GPU."""
+    import ctypes as C
+    from mxfp4_expert_matmul_amd._binding import _Weights
+    dll = lib.load_library()
+    buf = (C.c_uint8 * 64)()
+    p = C.cast(C.addressof(buf) + (-C.addressof(buf)) % 16, C.c_void_p).value  # 16-byte aligned
+    w = _Weights(p, None, p, p, p, p, p, p)
+    good = lib.Config(2048, 64, 8, 1024, 8)._c()
+    f = dll.k3moe_layer_forward_noalloc
+    assert f(None, C.byref(w), p, 1, p, None, None, None) == lib.K3MOE_EINVAL
+    assert f(C.byref(good), None, p, 1, p, None, None, None) == lib.K3MOE_EINVAL
+    assert f(C.byref(good), C.byref(w), p, 9, p, None, None, None) == lib.K3MOE_EINVAL   # T > max_tokens
+    assert f(C.byref(good), C.byref(w), None, 1, p, None, None, None) == lib.K3MOE_EINVAL
+    assert f(C.byref(good), C.byref(w), p, 1, p, p, None, None) == lib.K3MOE_EINVAL      # idx without gate
+    assert f(C.byref(good), C.byref(w), p, 5, p, None, None, None) == lib.K3MOE_EUNSUPPORTED  # T > 4
+    big = lib.Config(4096, 4096, 64, 4096, 4)._c()  # 4 MiB of h at T = 4
+    assert f(C.byref(big), C.byref(w), p, 4, p, None, None, None) == lib.K3MOE_EUNSUPPORTED
+    nodown = _Weights(p, None, p, p, p, p, p, None)
+    assert f(C.byref(good), C.byref(nodown), p, 1, p, None, None, None) == lib.K3MOE_EINVAL
+    assert f(C.byref(good), C.byref(w), p, 0, p, None, None, None) == lib.K3MOE_OK       # T = 0
