@@ -209,6 +209,52 @@ int k3o_topk_gates(const float *logits, int64_t T, int64_t E, int64_t k,
     return K3O_OK;
 }
 
+/* The selection-only bias reading of a router bias (the pages give the
+ * skewed workload's per-expert bias without saying where it enters; the
+ * plain reading adds it to the logits for both steps, the alternative uses
+ * it only to choose the experts, as aux-loss-free balancing biases do):
+ * per token, the k experts ranking first by sel_logits (order and NaN rule
+ * as in k3o_topk_gates), and gate_j = exp(r_j - m) / sum over the selected
+ * of exp(r - m), where r are the same experts' gate_logits (NaN counts as
+ * -inf) and m the largest of them, in fp64. */
+int k3o_topk_gates_split(const float *sel_logits, const float *gate_logits, int64_t T, int64_t E,
+                         int64_t k, int32_t *idx, double *gate)
+{
+    if (T < 0 || E <= 0 || k < 1 || k > E)
+        return K3O_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = sel_logits + t * E;
+        const float *raw = gate_logits + t * E;
+        int32_t *sel = idx + t * k;
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int64_t p = 0; p < j; ++p)
+                    if (sel[p] == e)
+                        taken = 1;
+                if (taken)
+                    continue;
+                if (best < 0 || ranks_before(row[e], e, row[best], best))
+                    best = e;
+            }
+            sel[j] = (int32_t)best;
+        }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < k; ++j)
+            if (logit_value(raw[sel[j]]) > m)
+                m = logit_value(raw[sel[j]]);
+        double sum = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            gate[t * k + j] = exp(logit_value(raw[sel[j]]) - m);
+            sum += gate[t * k + j];
+        }
+        for (int64_t j = 0; j < k; ++j)
+            gate[t * k + j] /= sum;
+    }
+    return K3O_OK;
+}
+
 /* ------------------------------------------------------------ expert */
 
 /* SiLU(z) = z / (1 + e^-z); for very negative z, e^-z overflows to +inf and

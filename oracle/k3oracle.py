@@ -62,6 +62,8 @@ def _load():
         lib.k3o_router_logits.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
         lib.k3o_topk_gates.restype = ctypes.c_int
         lib.k3o_topk_gates.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        lib.k3o_topk_gates_split.restype = ctypes.c_int
+        lib.k3o_topk_gates_split.argtypes = [_P, _P, _I64, _I64, _I64, _P, _P]
         lib.k3o_silu_array.restype = None
         lib.k3o_silu_array.argtypes = [_P, _I64, _P]
         lib.k3o_expert_ffn.restype = ctypes.c_int
@@ -168,13 +170,22 @@ def router_logits(x_bits: np.ndarray, router_w: np.ndarray,
     return out
 
 
-def topk_gates(logits: np.ndarray, k: int):
-    """idx [T][k] int32 (logit descending, index ascending) and fp64 gates."""
+def topk_gates(logits: np.ndarray, k: int, gate_logits: np.ndarray | None = None):
+    """idx [T][k] int32 (logit descending, index ascending) and fp64 gates.
+    With gate_logits, `logits` only choose the experts and the gates are the
+    softmax of the chosen experts' gate_logits (the selection-only bias)."""
     lg = _c(np.atleast_2d(logits), np.float32)
     T, E = lg.shape
     idx = np.empty((T, k), dtype=np.int32)
     gate = np.empty((T, k), dtype=np.float64)
-    _check(_load().k3o_topk_gates(_ptr(lg), T, E, int(k), _ptr(idx), _ptr(gate)), "topk_gates")
+    if gate_logits is None:
+        _check(_load().k3o_topk_gates(_ptr(lg), T, E, int(k), _ptr(idx), _ptr(gate)), "topk_gates")
+    else:
+        gl = _c(np.atleast_2d(gate_logits), np.float32)
+        if gl.shape != lg.shape:
+            raise ValueError("gate_logits must have the shape of logits")
+        _check(_load().k3o_topk_gates_split(_ptr(lg), _ptr(gl), T, E, int(k), _ptr(idx),
+                                            _ptr(gate)), "topk_gates_split")
     return idx, gate
 
 
@@ -251,8 +262,16 @@ def experts_forward(x_bits: np.ndarray, idx: np.ndarray, gate: np.ndarray,
     return y
 
 
-def layer_forward(x_bits, router_w, bias, experts, k: int):
-    """Whole layer. Returns dict(y64, y32, idx, gate, logits)."""
+def layer_forward(x_bits, router_w, bias, experts, k: int, bias_select_only: bool = False):
+    """Whole layer. Returns dict(y64, y32, idx, gate, logits). With
+    bias_select_only the bias ranks the experts but the gates come from the
+    unbiased logits (and `logits` are the unbiased ones)."""
+    if bias_select_only and bias is not None:
+        logits = router_logits(x_bits, router_w, None)
+        idx, gate = topk_gates(router_logits(x_bits, router_w, bias), k, gate_logits=logits)
+        y = experts_forward(x_bits, idx, gate, experts, n_experts=np.shape(router_w)[0])
+        return {"y64": y, "y32": y.astype(np.float32), "idx": idx, "gate": gate,
+                "logits": logits}
     logits = router_logits(x_bits, router_w, bias)
     idx, gate = topk_gates(logits, k)
     y = experts_forward(x_bits, idx, gate, experts, n_experts=np.shape(router_w)[0])

@@ -189,6 +189,56 @@ def test_topk_nan_logits_count_as_minus_inf():
     assert list(idx[0]) == [0, 1] and np.all(np.isnan(gate))
 
 
+def test_selection_only_bias():
+    """The selection-only reading of a router bias: the bias ranks the
+    experts, the gates are a softmax of the unbiased logits of the chosen
+    ones. Pinned by: zero bias gives the default mode exactly; the selection
+    is the brute-force top-k of the biased logits; the gates do not change
+    under any bias that keeps the selection, nor under a shift of all
+    logits; x = 0 gives gates 1/k; and the default mode's gates follow from
+    these by g_default_j = g_j e^(b_j) / sum_i g_i e^(b_i)."""
+    rng = np.random.default_rng(23)
+    for trial in range(120):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        raw = (rng.integers(-2, 3, E) if trial % 3 == 0 else rng.standard_normal(E)).astype(np.float32)
+        bias = (0.7 * rng.standard_normal(E)).astype(np.float32)
+        sel = raw + bias  # fp32, as the router adds it
+        idx, g = oracle.topk_gates(sel[None, :], k, gate_logits=raw[None, :])
+        assert list(idx[0]) == _brute_topk(sel, k)
+        i0, g0 = oracle.topk_gates(raw[None, :], k, gate_logits=raw[None, :])
+        d0, dg = oracle.topk_gates(raw[None, :], k)
+        assert np.array_equal(i0, d0) and np.array_equal(g0, dg)
+        # another bias with the same selection: the gates stay
+        shift = np.zeros(E, np.float32)
+        shift[idx[0]] = 0.25  # raising the chosen ones keeps them chosen
+        _, g2 = oracle.topk_gates((sel + shift)[None, :], k, gate_logits=raw[None, :])
+        assert np.allclose(g2, g, rtol=1e-14, atol=0)
+        # (the shifted fp32 logits are rounded again: differences move by ~2^-24)
+        _, g3 = oracle.topk_gates(sel[None, :], k, gate_logits=(raw + np.float32(0.5))[None, :])
+        assert np.allclose(g3, g, rtol=1e-6, atol=1e-12)
+        # the default mode on the biased logits, from these gates
+        di, dgb = oracle.topk_gates(sel[None, :], k)
+        assert np.array_equal(di, idx)
+        w = g[0] * np.exp(sel[idx[0]].astype(np.float64) - raw[idx[0]].astype(np.float64))
+        assert np.allclose(dgb[0], w / w.sum(), rtol=1e-12, atol=1e-15)
+    cfg = synth.CONFIGS[1]
+    bias = synth.skew_bias(4, cfg.E)
+    x0 = np.zeros((1, cfg.d), dtype=np.uint16)
+    wr = synth.gen_router_w(cfg)
+    r = oracle.layer_forward(x0, wr, bias, synth.ExpertSource(cfg, synth.gen_weights(cfg)), cfg.k,
+                             bias_select_only=True)
+    assert list(r["idx"][0]) == list(np.argsort(-bias.astype(np.float64), kind="stable")[:cfg.k])
+    assert np.all(r["gate"] == 1.0 / cfg.k)
+    # zero bias: the whole layer equals the default mode bit for bit
+    x = synth.gen_x(cfg, T=3)
+    src = synth.ExpertSource(cfg, synth.gen_weights(cfg))
+    zero = np.zeros(cfg.E, np.float32)
+    a = oracle.layer_forward(x, wr, zero, src, cfg.k, bias_select_only=True)
+    b = oracle.layer_forward(x, wr, zero, src, cfg.k)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["y64"], b["y64"])
+
+
 def test_gates_sum_to_one_and_bias_selects():
     cfg = synth.CONFIGS[1]
     E, k = cfg.E, cfg.k
