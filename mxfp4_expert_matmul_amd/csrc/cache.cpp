@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "k3moe.h"
+#include "lru.h"
 
 namespace {
 
@@ -54,15 +55,8 @@ struct k3moe_cache {
   int32_t* sidx_dev;   // [max_tokens][k] the same selection as slot ids
   int32_t* idx_host;   // pinned copies
   int32_t* sidx_host;
-  std::vector<int32_t> slot_of;    // [E]: slot holding expert e, or -1
-  std::vector<int32_t> expert_in;  // [n_slots]: expert in slot s, or -1
-  std::vector<int64_t> last_use;   // [n_slots]: stamp of the last call that used slot s (0: never)
-  std::vector<int64_t> seen;       // [E]: stamp of the last call that routed to expert e
-  std::vector<int64_t> fwd_use;    // [n_slots]: stamp of the last forward that used slot s
-  std::vector<uint8_t> pre;        // [n_slots]: brought in by a prefetch, not used since
-  std::vector<int32_t> uniq;       // scratch: distinct experts of a call
-  int64_t stamp;                   // counts every forward past the routing and every prefetch
-  int64_t last_fwd;                // stamp of the last forward that enqueued its kernels (0: none)
+  k3::ExpertLru lru;               // which slot holds which expert, and the replacement rule
+  std::vector<k3::SlotCopy> copies;  // scratch: the copies a call or prefetch plans
   hipEvent_t pf_ev;                // recorded after the last prefetch's copies
   bool pf_pending;                 // the next forward must wait for pf_ev
   int64_t calls, hits, misses, bytes_in;  // completed calls and their experts
@@ -95,15 +89,6 @@ void release(k3moe_cache* c) {
   (void)hipHostFree(c->sidx_host);
 }
 
-// Forget every resident expert (after a failed call the arena's contents are
-// not known).
-void forget(k3moe_cache* c) {
-  std::fill(c->slot_of.begin(), c->slot_of.end(), -1);
-  std::fill(c->expert_in.begin(), c->expert_in.end(), -1);
-  std::fill(c->last_use.begin(), c->last_use.end(), 0);
-  std::fill(c->pre.begin(), c->pre.end(), 0);
-}
-
 // Copy expert e into slot v on stream st (the six tensors); the caller
 // updates the residency tables.
 hipError_t copy_in(k3moe_cache* c, int32_t e, int32_t v, hipStream_t st) {
@@ -116,21 +101,13 @@ hipError_t copy_in(k3moe_cache* c, int32_t e, int32_t v, hipStream_t st) {
   return hipSuccess;
 }
 
-// Put expert e in slot v (evicting what v held).
-void place(k3moe_cache* c, int32_t e, int32_t v) {
-  const int32_t old = c->expert_in[(size_t)v];
-  if (old >= 0) c->slot_of[(size_t)old] = -1;
-  c->expert_in[(size_t)v] = e;
-  c->slot_of[(size_t)e] = v;
-}
-
 // A failed forward or prefetch: wait for whatever it enqueued on st (so no
 // copy of it is still in flight when another stream reuses a slot), clear the
 // error and forget every resident expert.
 int fail(k3moe_cache* c, int rc, hipStream_t st) {
   (void)hipStreamSynchronize(st);
   (void)hipGetLastError();
-  forget(c);
+  c->lru.forget();
   return rc;
 }
 
@@ -211,15 +188,10 @@ int k3moe_cache_create(const k3moe_config* cfg, const k3moe_host_weights* w, int
     delete c;
     return rc;
   }
-  c->slot_of.assign((size_t)cfg->n_experts, -1);
-  c->expert_in.assign((size_t)n_slots, -1);
-  c->last_use.assign((size_t)n_slots, 0);
-  c->seen.assign((size_t)cfg->n_experts, 0);
-  c->uniq.reserve((size_t)n_slots);
-  c->fwd_use.assign((size_t)n_slots, 0);
-  c->pre.assign((size_t)n_slots, 0);
-  c->stamp = c->calls = c->hits = c->misses = c->bytes_in = 0;
-  c->last_fwd = c->prefetched = c->pf_hits = 0;
+  c->lru.reset(cfg->n_experts, n_slots);
+  c->copies.reserve((size_t)n_slots);
+  c->calls = c->hits = c->misses = c->bytes_in = 0;
+  c->prefetched = c->pf_hits = 0;
   c->pf_pending = false;
   if (hipEventCreateWithFlags(&c->pf_ev, hipEventDisableTiming) != hipSuccess) {
     c->pf_ev = nullptr;
@@ -266,7 +238,6 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
   Guard guard(c->device);
   if (!guard.ok) return K3MOE_EHIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t E = c->cfg.n_experts;
   const size_t P = (size_t)T * c->cfg.top_k;
 
   // 1. route over all experts and read the selection back
@@ -278,17 +249,12 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     return fail(c, K3MOE_EHIP, st);
   }
 
-  // 2. the call's distinct experts; refuse before changing anything if they
-  // cannot all be resident at once
-  const int64_t call = ++c->stamp;
-  c->uniq.clear();
-  for (size_t p = 0; p < P; ++p) {
-    const int32_t e = c->idx_host[p];
-    if (e < 0 || e >= E || c->seen[(size_t)e] == call) continue;
-    c->seen[(size_t)e] = call;
-    if ((int32_t)c->uniq.size() == c->n_slots) return K3MOE_EUNSUPPORTED;
-    c->uniq.push_back(e);
-  }
+  // 2. plan the call: its distinct experts, the hits, and for each miss the
+  // least recently used slot the call does not use. Refused, with nothing
+  // changed, if they cannot all be resident at once.
+  int64_t hits = 0, misses = 0, pf_hits = 0;
+  if (!c->lru.plan_forward(c->idx_host, P, c->copies, hits, misses, pf_hits))
+    return K3MOE_EUNSUPPORTED;
   // copies of an earlier prefetch (possibly on another stream) land before
   // this call copies into, or reads, any slot
   if (c->pf_pending) {
@@ -298,46 +264,14 @@ int k3moe_cache_forward(k3moe_cache* c, const void* x, int32_t T, float* y, int3
     }
     c->pf_pending = false;
   }
-  int64_t hits = 0, misses = 0, pf_hits = 0;
-  // hits first, so no expert this call needs is evicted for another
-  for (int32_t e : c->uniq) {
-    const int32_t s = c->slot_of[(size_t)e];
-    if (s >= 0) {
-      c->last_use[(size_t)s] = call;
-      ++hits;
-      pf_hits += c->pre[(size_t)s];
-    }
-  }
-  // 3. misses: the least recently used slot not used by this call (free
-  // slots have last_use 0); copy the expert in on the call's stream
-  for (int32_t e : c->uniq) {
-    if (c->slot_of[(size_t)e] >= 0) continue;
-    int32_t v = -1;
-    for (int32_t s = 0; s < c->n_slots; ++s)
-      if (c->last_use[(size_t)s] < call && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v]))
-        v = s;
-    // a victim exists: fewer distinct experts than slots are in use by this call
-    place(c, e, v);
-    if (copy_in(c, e, v, st) != hipSuccess) {
+  // 3. the misses' copies, on the call's stream
+  for (const k3::SlotCopy& cp : c->copies)
+    if (copy_in(c, cp.expert, cp.slot, st) != hipSuccess) {
       (void)hipGetLastError();
       return fail(c, K3MOE_EHIP, st);
     }
-    c->last_use[(size_t)v] = call;
-    ++misses;
-  }
-  // every slot this call uses: a plain resident from now on, and off limits
-  // to prefetches until a later forward is enqueued
-  for (int32_t e : c->uniq) {
-    const int32_t s = c->slot_of[(size_t)e];
-    c->pre[(size_t)s] = 0;
-    c->fwd_use[(size_t)s] = call;
-  }
-  c->last_fwd = call;
   // 4. the selection renamed to slots (dropped pairs stay out of range)
-  for (size_t p = 0; p < P; ++p) {
-    const int32_t e = c->idx_host[p];
-    c->sidx_host[p] = (e >= 0 && e < E) ? c->slot_of[(size_t)e] : -1;
-  }
+  c->lru.rename(c->idx_host, P, c->sidx_host);
   if (hipMemcpyAsync(c->sidx_dev, c->sidx_host, P * 4, hipMemcpyHostToDevice, st) != hipSuccess) {
     (void)hipGetLastError();
     return fail(c, K3MOE_EHIP, st);
@@ -369,50 +303,22 @@ int k3moe_cache_prefetch(k3moe_cache* c, const int32_t* experts, int32_t n, void
   Guard guard(c->device);
   if (!guard.ok) return K3MOE_EHIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t pst = ++c->stamp;
   // slots a prefetch may fill: not used by the last forward (its kernels may
-  // still run) and not taken (filled or refreshed) by this prefetch
-  auto eligible = [&](int32_t s) {
-    return (c->last_fwd == 0 || c->fwd_use[(size_t)s] != c->last_fwd) && c->last_use[(size_t)s] < pst;
-  };
-  // distinct listed experts: the resident ones in such slots are refreshed
-  // (which takes their slots), the ones not resident need a slot each;
-  // refuse before changing anything if too few slots are left for them
-  c->uniq.clear();
-  int32_t refreshed = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t e = experts[i];
-    if (c->seen[(size_t)e] == pst) continue;
-    c->seen[(size_t)e] = pst;
-    const int32_t s = c->slot_of[(size_t)e];
-    if (s < 0)
-      c->uniq.push_back(e);
-    else if (eligible(s))
-      ++refreshed;
-  }
-  int32_t free_slots = 0;
-  for (int32_t s = 0; s < c->n_slots; ++s) free_slots += eligible(s) ? 1 : 0;
-  if ((int32_t)c->uniq.size() > free_slots - refreshed) return K3MOE_EUNSUPPORTED;
-  for (int32_t i = 0; i < n; ++i) {  // refresh the resident ones
-    const int32_t s = c->slot_of[(size_t)experts[i]];
-    if (s >= 0 && eligible(s)) c->last_use[(size_t)s] = pst;
+  // still run) and not taken by this prefetch; refused, with nothing
+  // changed, if too few are left for the listed experts that are not
+  // resident
+  const k3::ExpertLru::PrefetchPlan plan = c->lru.plan_prefetch(experts, n, c->copies);
+  if (plan == k3::ExpertLru::kRefused) return K3MOE_EUNSUPPORTED;
+  if (plan == k3::ExpertLru::kBroken) {
+    c->pf_pending = false;
+    return fail(c, K3MOE_EUNSUPPORTED, st);
   }
   int64_t copied = 0;
-  for (int32_t e : c->uniq) {
-    int32_t v = -1;
-    for (int32_t s = 0; s < c->n_slots; ++s)
-      if (eligible(s) && (v < 0 || c->last_use[(size_t)s] < c->last_use[(size_t)v])) v = s;
-    if (v < 0) {  // cannot happen after the count above; never index with it
-      c->pf_pending = false;
-      return fail(c, K3MOE_EUNSUPPORTED, st);
-    }
-    place(c, e, v);
-    if (copy_in(c, e, v, st) != hipSuccess) {
+  for (const k3::SlotCopy& cp : c->copies) {
+    if (copy_in(c, cp.expert, cp.slot, st) != hipSuccess) {
       c->pf_pending = false;
       return fail(c, K3MOE_EHIP, st);
     }
-    c->last_use[(size_t)v] = pst;
-    c->pre[(size_t)v] = 1;
     ++copied;
   }
   if (hipEventRecord(c->pf_ev, st) != hipSuccess) {
