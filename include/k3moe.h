@@ -72,16 +72,27 @@ typedef struct k3moe k3moe;  /* opaque handle */
  * (32-bit offsets into the prefill activation planes; at d=7168, k=16,
  * f=2048 that is up to 32768 tokens per call). Anything else returns
  * K3MOE_EINVAL (malformed: non-positive sizes, d or f not a multiple of 32,
- * k > E, flags != 0) or K3MOE_EUNSUPPORTED (well-formed but beyond these
- * limits). */
+ * k > E, unknown flags) or K3MOE_EUNSUPPORTED (well-formed but beyond
+ * these limits). */
 typedef struct {
   int32_t d_model;     /* d: hidden size */
   int32_t n_experts;   /* E: routed experts */
   int32_t top_k;       /* k: experts per token */
   int32_t d_ff;        /* f: expert FFN width */
   int32_t max_tokens;  /* largest T any later call may pass; sizes the workspace */
-  uint32_t flags;      /* reserved, must be 0 */
+  uint32_t flags;      /* 0 or K3MOE_FLAG_BIAS_SELECT_ONLY; other bits are invalid */
 } k3moe_config;
+
+/* flags: where the router bias enters. By default (flags = 0) router_b is
+ * added to every logit before both the selection and the gates (the plain
+ * reading of "a per-expert router bias"). With K3MOE_FLAG_BIAS_SELECT_ONLY
+ * it only ranks the experts: the top k are chosen by l[e] + bias[e] (fp32
+ * add, same ties and NaN rule), and the gates are the softmax of the chosen
+ * experts' unbiased l[e] about their largest (the alternative reading, as
+ * aux-loss-free load-balancing biases are used). The pages give the skewed
+ * workload's bias but not where it enters. k3moe_route's logits output is
+ * then the unbiased l. Without a bias the two modes are the same. */
+#define K3MOE_FLAG_BIAS_SELECT_ONLY 1u
 
 /* Layer weights (HOST struct of DEVICE pointers). BORROWED: they must stay
  * valid and unchanged until k3moe_destroy; the library never writes or

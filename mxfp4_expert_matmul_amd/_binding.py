@@ -17,6 +17,7 @@ K3MOE_EINVAL = -1
 K3MOE_ENOMEM = -2
 K3MOE_EHIP = -3
 K3MOE_EUNSUPPORTED = -4
+K3MOE_FLAG_BIAS_SELECT_ONLY = 1  # k3moe_config.flags: the router bias only ranks the experts
 
 
 class K3MoEError(RuntimeError):

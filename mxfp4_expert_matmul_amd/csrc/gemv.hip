@@ -125,7 +125,8 @@ template <int XC, int V>  // V: logits per lane in the selection, E <= 64 V
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const uint16_t* __restrict__ x, int d, int f, int k, int E, const uint8_t* __restrict__ gq,
     const uint8_t* __restrict__ gs, const uint8_t* __restrict__ uq, const uint8_t* __restrict__ us,
-    const float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate,
+    const float* __restrict__ logits, const float* __restrict__ sel_bias,
+    int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ h32) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [4][512 * XC]
   __shared__ uint64_t cand[4][64];
@@ -149,10 +150,11 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   }
   int e;
   if (logits) {
-    const uint64_t mine = topk_token<V>(logits + (size_t)t * E, E, k, cand[wave], sel[wave]);
+    const float* row = logits + (size_t)t * E;
+    const uint64_t mine = topk_token<V>(row, E, k, cand[wave], sel[wave], sel_bias);
     e = ~__builtin_amdgcn_readlane((int)(uint32_t)mine, j);  // selection j's expert
     if (j == 0 && blockIdx.y == 0 && wave == 0) {
-      const float g = topk_gate_of(mine, k);
+      const float g = sel_bias ? topk_gate_unbiased(mine, k, row) : topk_gate_of(mine, k);
       if (lane < k) {
         idx[(size_t)t * k + lane] = topk_key_index(mine);
         gate[(size_t)t * k + lane] = g;
@@ -397,14 +399,14 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
 static size_t gateup_lds_bytes(int d) { return (size_t)4 * 1024 * gu_x_copies(d); }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const float* logits, int32_t* idx, float* gate, float* h32,
-                              hipStream_t st) {
+                              const float* logits, const float* sel_bias, int32_t* idx,
+                              float* gate, float* h32, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const dim3 g1(T * s.k, (s.f / 16 + 3) / 4);
   const size_t lds = gateup_lds_bytes(s.d);
 #define K3_GATEUP(XC, V)                                                                       \
   hipLaunchKernelGGL((gemv_gateup_kernel<XC, V>), g1, dim3(256), lds, st, x, s.d, s.f, s.k,   \
-                     s.E, w.gate_q, w.gate_s, w.up_q, w.up_s, logits, idx, gate, h32)
+                     s.E, w.gate_q, w.gate_s, w.up_q, w.up_s, logits, sel_bias, idx, gate, h32)
 #define K3_GATEUP_V(XC)                                                                        \
   do {                                                                                         \
     if (s.E <= 1024)                                                                           \

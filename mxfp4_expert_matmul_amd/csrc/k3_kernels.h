@@ -38,8 +38,10 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
                                 hipStream_t st);
 // three-term bf16 split of the router weights, w3 = [hi | mid | lo] each [E][d]
 hipError_t launch_router_split(const float* wr, int E, int d, uint16_t* w3, hipStream_t st);
-hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,
-                       hipStream_t st);
+// sel_bias != NULL: the selection-only bias (ranks logits + sel_bias, gates
+// from the logits alone)
+hipError_t launch_topk(const float* logits, int T, const Shape& s, const float* sel_bias,
+                       int32_t* idx, float* gate, hipStream_t st);
 
 // group.hip
 hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* counts,
@@ -51,8 +53,8 @@ hipError_t launch_group(const int32_t* idx, int T, const Shape& s, int32_t* coun
 // token's logits inside the kernel, which also writes idx and gate; else idx
 // is the routing (gate unused)
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
-                              const float* logits, int32_t* idx, float* gate, float* h32,
-                              hipStream_t st);
+                              const float* logits, const float* sel_bias, int32_t* idx,
+                              float* gate, float* h32, hipStream_t st);
 hipError_t launch_gemv_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* idx,
                             const float* gate, const float* h32, float* y, hipStream_t st);
 // once per handle: raise the dynamic LDS limits the decode kernels of shape s need

@@ -36,7 +36,7 @@ struct Plan {
 
 int check_config(const k3moe_config* c) {
   if (!c) return K3MOE_EINVAL;
-  if (c->flags != 0u) return K3MOE_EINVAL;
+  if ((c->flags & ~K3MOE_FLAG_BIAS_SELECT_ONLY) != 0u) return K3MOE_EINVAL;
   if (c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 ||
       c->max_tokens <= 0)
     return K3MOE_EINVAL;
@@ -151,6 +151,15 @@ void profile_release(k3moe* h) {
   h->prof_cap = 0;
 }
 
+// The router bias as the logit kernels see it (added to every logit) and as
+// the top-k sees it (added only to rank: the selection-only bias).
+const float* logit_bias(const k3moe_config& c, const float* b) {
+  return (c.flags & K3MOE_FLAG_BIAS_SELECT_ONLY) ? nullptr : b;
+}
+const float* select_bias(const k3moe_config& c, const float* b) {
+  return (c.flags & K3MOE_FLAG_BIAS_SELECT_ONLY) ? b : nullptr;
+}
+
 Shape shape_of(const k3moe* h) {
   return Shape{h->cfg.d_model, h->cfg.n_experts, h->cfg.top_k, h->cfg.d_ff};
 }
@@ -185,11 +194,14 @@ int run_router(k3moe* h, const uint16_t* x, int T, float* logits, int32_t* idx, 
                hipStream_t st, bool with_topk = true) {
   const Shape s = shape_of(h);
   hipError_t e = stage(h, K3MOE_STAGE_ROUTER_LOGITS, st, [&] {
-    return k3::launch_router_logits(x, T, s, h->w.router_w, h->wr3, h->w.router_b, logits, st);
+    return k3::launch_router_logits(x, T, s, h->w.router_w, h->wr3,
+                                    logit_bias(h->cfg, h->w.router_b), logits, st);
   });
   if (e != hipSuccess) return K3MOE_EHIP;
   if (!with_topk) return K3MOE_OK;
-  e = stage(h, K3MOE_STAGE_TOPK, st, [&] { return k3::launch_topk(logits, T, s, idx, gate, st); });
+  e = stage(h, K3MOE_STAGE_TOPK, st, [&] {
+    return k3::launch_topk(logits, T, s, select_bias(h->cfg, h->w.router_b), idx, gate, st);
+  });
   return hip_status(e);
 }
 
@@ -203,7 +215,8 @@ int run_experts(k3moe* h, const uint16_t* x, int T, int32_t* idx, float* gate, f
   hipError_t e;
   if (T <= k3::kGemvMaxT) {
     e = stage(h, K3MOE_STAGE_GATEUP, st, [&] {
-      return k3::launch_gemv_gateup(x, T, s, w, logits, idx, gate, h->h32, st);
+      return k3::launch_gemv_gateup(x, T, s, w, logits, select_bias(h->cfg, h->w.router_b), idx,
+                                    gate, h->h32, st);
     });
     if (e != hipSuccess) return K3MOE_EHIP;
     e = stage(h, K3MOE_STAGE_DOWN, st,
@@ -536,8 +549,11 @@ int k3moe_layer_forward_noalloc(const k3moe_config* cfg, const k3moe_weights* w,
   const k3::ExpertWeights ew{w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  hipError_t e = k3::launch_router_logits(xb, T, s, w->router_w, nullptr, w->router_b, logits, st);
-  if (e == hipSuccess) e = k3::launch_gemv_gateup(xb, T, s, ew, logits, idx, gate, h32, st);
+  hipError_t e = k3::launch_router_logits(xb, T, s, w->router_w, nullptr,
+                                          logit_bias(*cfg, w->router_b), logits, st);
+  if (e == hipSuccess)
+    e = k3::launch_gemv_gateup(xb, T, s, ew, logits, select_bias(*cfg, w->router_b), idx, gate,
+                               h32, st);
   if (e == hipSuccess) e = k3::launch_gemv_down(T, s, ew, idx, gate, h32, y, st);
   return hip_status(e);
 }

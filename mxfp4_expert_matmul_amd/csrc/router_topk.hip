@@ -230,31 +230,36 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
 
 template <int V>  // logits per lane: E <= 64 * V
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int32_t* __restrict__ idx,
+                                                   int k, const float* __restrict__ sel_bias,
+                                                   int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
   __shared__ uint64_t cand[4][64];
   __shared__ uint64_t sel[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;  // waves work independently (wave-private LDS, no barrier)
-  const uint64_t mine = topk_token<V>(logits + (size_t)t * E, E, k, cand[wv], sel[wv]);
-  const float g = topk_gate_of(mine, k);
+  const float* row = logits + (size_t)t * E;
+  const uint64_t mine = topk_token<V>(row, E, k, cand[wv], sel[wv], sel_bias);
+  const float g = sel_bias ? topk_gate_unbiased(mine, k, row) : topk_gate_of(mine, k);
   if (lane < k) {
     idx[(size_t)t * k + lane] = topk_key_index(mine);
     gate[(size_t)t * k + lane] = g;
   }
 }
 
-hipError_t launch_topk(const float* logits, int T, const Shape& s, int32_t* idx, float* gate,
-                       hipStream_t st) {
+hipError_t launch_topk(const float* logits, int T, const Shape& s, const float* sel_bias,
+                       int32_t* idx, float* gate, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   dim3 grid((T + 3) / 4);
   if (s.E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, st, logits, T, s.E, s.k, sel_bias, idx,
+                       gate);
   else if (s.E <= 1024)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, logits, T, s.E, s.k, sel_bias, idx,
+                       gate);
   else
-    hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, st, logits, T, s.E, s.k, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, st, logits, T, s.E, s.k, sel_bias, idx,
+                       gate);
   return hipGetLastError();
 }
 

@@ -124,16 +124,19 @@ __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand,
 }
 
 // Keys of token row `row` (E logits, V per lane), then their top k: lane
-// r < k returns selection r.
+// r < k returns selection r. With sel_bias (the selection-only bias) the
+// keys rank row[e] + sel_bias[e], added in fp32.
 template <int V>  // logits per lane: E <= 64 * V
 __device__ __forceinline__ uint64_t topk_token(const float* row, int E, int k, uint64_t* cand,
-                                               uint64_t* sel) {
+                                               uint64_t* sel, const float* sel_bias = nullptr) {
   const int lane = threadIdx.x & 63;
   uint64_t key[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int e = lane + 64 * j;
-    key[j] = (e < E) ? topk_key(row[e], e) : 0ull;  // 0 is below every real key
+    float v = 0.0f;
+    if (e < E) v = sel_bias ? row[e] + sel_bias[e] : row[e];
+    key[j] = (e < E) ? topk_key(v, e) : 0ull;  // 0 is below every real key
   }
   return select_topk<V>(key, k, cand, sel);
 }
@@ -143,6 +146,21 @@ __device__ __forceinline__ float topk_gate_of(uint64_t mine, int k) {
   const int lane = threadIdx.x & 63;
   const float v = topk_key_value(mine);
   const float vmax = __shfl(v, 0, 64);
+  const float w = (lane < k) ? expf(v - vmax) : 0.0f;
+  return w / wave_sum_dpp(w);
+}
+
+// Gate of lane r < k's selection under the selection-only bias: the softmax
+// of the selected experts' unbiased logits row[e] (NaN counts as -inf) about
+// their largest.
+__device__ __forceinline__ float topk_gate_unbiased(uint64_t mine, int k, const float* row) {
+  const int lane = threadIdx.x & 63;
+  float v = -INFINITY;
+  if (lane < k) {
+    v = row[topk_key_index(mine)];
+    if (v != v) v = -INFINITY;
+  }
+  const float vmax = wave_max(v);
   const float w = (lane < k) ? expf(v - vmax) : 0.0f;
   return w / wave_sum_dpp(w);
 }

@@ -122,3 +122,12 @@ def test_noalloc_validates_before_any_device_call(lib):
     nodown = _Weights(p, None, p, p, p, p, p, None)
     assert f(C.byref(good), C.byref(nodown), p, 1, p, None, None, None) == lib.K3MOE_EINVAL
     assert f(C.byref(good), C.byref(w), p, 0, p, None, None, None) == lib.K3MOE_OK       # T = 0
+
+
+def test_flags_validation(lib):
+    """flags: 0 and the selection-only bias bit are valid, any other bit is
+    refused."""
+    assert lib.k3moe_workspace_bytes(lib.Config(128, 8, 2, 256, 1, 0)) > 0
+    assert lib.k3moe_workspace_bytes(lib.Config(128, 8, 2, 256, 1, lib.K3MOE_FLAG_BIAS_SELECT_ONLY)) > 0
+    for bad in (2, 4, 3, 1 << 31):
+        assert lib.k3moe_workspace_bytes(lib.Config(128, 8, 2, 256, 1, bad)) == lib.K3MOE_EINVAL

@@ -51,8 +51,8 @@ class Small:
         self.dw = k3m.pack_layer_weights(rowmajor, cfg.E, cfg.d, cfg.f)
 
 
-def _layer(k3, cfg, dw, max_tokens):
-    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, max_tokens)
+def _layer(k3, cfg, dw, max_tokens, flags=0):
+    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, max_tokens, flags)
     return k3.Layer(c, dw, 0)
 
 
@@ -60,15 +60,21 @@ def _x_dev(x_bits):
     return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def _run_and_check(k3, layer, cfg, x_bits, src, wr, bias, tokens=None, label=""):
+def _run_and_check(k3, layer, cfg, x_bits, src, wr, bias, tokens=None, label="",
+                   select_only=False):
     """Full forward on the GPU; routing check on every token, output check on
-    `tokens` (all if None)."""
+    `tokens` (all if None). select_only: the layer uses the selection-only
+    bias (the bias ranks the experts, the gates come from unbiased logits)."""
     T = x_bits.shape[0]
     y, idx, gate = layer.forward(_x_dev(x_bits))
     torch.cuda.synchronize()
     y, idx, gate = y.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy()
     logits = oracle.router_logits(x_bits, wr, bias)
-    ridx, rgate = oracle.topk_gates(logits, cfg.k)
+    if select_only:
+        ridx, rgate = oracle.topk_gates(logits, cfg.k,
+                                        gate_logits=oracle.router_logits(x_bits, wr, None))
+    else:
+        ridx, rgate = oracle.topk_gates(logits, cfg.k)
     excused, log = compare_routing(idx, logits, ridx, cfg.k)
     for line in log:
         _say(f"[{label}] {line}")
@@ -328,6 +334,36 @@ def test_nan_scale_block_propagates(k3, T):
     assert n_nan > 0
     _say(f"[NaN scale T={T}] {n_nan} NaN outputs as expected; finite max|err|/rms = {ratio:.3e}")
     layer.close()
+
+
+@pytest.mark.parametrize("T", [1, 3, 40, 96])
+def test_selection_only_bias(k3, T):
+    """K3MOE_FLAG_BIAS_SELECT_ONLY with the skewed bias 2(rank+1)^-1.2 at the
+    small shape: the bias ranks the experts, the gates are the softmax of the
+    unbiased logits of the chosen ones. Routing, gates and outputs against the
+    oracle's selection-only mode, on the fused decode top-k (T <= 4) and the
+    top-k kernel with the grouped GEMM; the default mode on the same layer
+    chooses the same experts with other gates."""
+    cfg = synth.LayerConfig("small_skew_select_only", 2048, 64, 8, 1024, 96, 5, skew_bias=True)
+    s = Small(cfg, 96)
+    sel = _layer(k3, cfg, s.dw, 96, flags=k3.K3MOE_FLAG_BIAS_SELECT_ONLY)
+    x = synth.gen_x(cfg, T=T, stream=21)
+    _, idx, gate = _run_and_check(k3, sel, cfg, x, s.src, s.wr, s.bias, select_only=True,
+                                  label=f"select-only bias T={T}")
+    both = _layer(k3, cfg, s.dw, 96)
+    _, idx2, gate2 = both.forward(_x_dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx, idx2.cpu().numpy())
+    assert np.max(np.abs(gate - gate2.cpu().numpy())) > 1e-3  # the bias no longer reaches the gates
+    logits = torch.empty((T, cfg.E), dtype=torch.float32, device="cuda")
+    i3 = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    g3 = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    k3.k3moe_route(sel.handle, _x_dev(x), i3, g3, logits)
+    torch.cuda.synchronize()
+    raw = oracle.router_logits(x, s.wr, None)  # the route step reports unbiased logits
+    assert np.max(np.abs(logits.cpu().numpy() - raw)) < 1e-4
+    sel.close()
+    both.close()
 
 
 @pytest.mark.parametrize("code_byte", [0x00, 0x88])
@@ -679,6 +715,24 @@ def test_k3_prefill_4096_skewed(k3, big_layers):
     tokens = _sample_tokens(ridx, cfg.E, 64, cfg.seed, "k3 prefill 4096 skew")
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
                    label="k3 prefill 4096 skew")
+
+
+@pytest.mark.timeout(600)
+def test_k3_prefill_4096_select_only_bias(k3, big_layers):
+    """The long skewed prefill with the bias read as selection-only: routing
+    on every token, outputs on 16 sampled tokens."""
+    _say("case k3 prefill T=4096 skewed, selection-only bias")
+    st = big_layers(4, 4096)
+    cfg = st["cfg"]
+    layer = _layer(k3, cfg, st["dw"], cfg.T, flags=k3.K3MOE_FLAG_BIAS_SELECT_ONLY)
+    x = synth.gen_x(cfg)
+    ridx, _ = oracle.topk_gates(oracle.router_logits(x, st["wr"], st["bias"]), cfg.k)
+    tokens = _sample_tokens(ridx, cfg.E, 16, cfg.seed + 100, "k3 prefill 4096 select-only")
+    try:
+        _run_and_check(k3, layer, cfg, x, st["src"], st["wr"], st["bias"], tokens=tokens,
+                       select_only=True, label="k3 prefill 4096 select-only")
+    finally:
+        layer.close()
 
 
 @pytest.mark.timeout(900)
