@@ -218,6 +218,22 @@ int k3moe_experts_forward(k3moe* h, const void* x, int32_t T,
 int k3moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t R, int32_t K,
                      uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream);
 
+/* The same rearrangement from row-major matrices in HOST memory (codes
+ * [n][R][K/2], scales [n][R][K/32], pinned or pageable) into the tiled
+ * DEVICE tensors tiled_codes / tiled_scales (16-byte aligned, sizes as for
+ * k3moe_pack_mxfp4), on the current HIP device: the way to load a
+ * checkpoint's experts. The matrices cross PCIe a chunk at a time through a
+ * device staging buffer of at most 32 MiB (at least one matrix), so loading
+ * needs the tiled tensors plus that buffer, never a second full copy.
+ * Enqueued on `stream`, then synchronised with it: returns once the tiled
+ * tensors are written and the staging buffer is freed. K3MOE_EINVAL for bad
+ * arguments, K3MOE_ENOMEM if the staging buffer cannot be allocated,
+ * K3MOE_EHIP if a copy or launch fails (the tiled tensors are then
+ * incomplete). */
+int k3moe_pack_mxfp4_from_host(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t R,
+                               int32_t K, uint8_t* tiled_codes, uint8_t* tiled_scales,
+                               void* stream);
+
 /* Bytes of tiled scales for n matrices of R x K (0 if the shape is invalid). */
 int64_t k3moe_tiled_scale_bytes(int32_t n, int32_t R, int32_t K);
 

@@ -12,5 +12,6 @@ from ._binding import (  # noqa: F401
     K3MoEError, Config, Layer, CachedLayer, load_library, library_path,
     k3moe_create, k3moe_destroy, k3moe_status_str, k3moe_workspace_bytes,
     k3moe_layer_forward, k3moe_layer_forward_noalloc, k3moe_route, k3moe_group, k3moe_experts_forward,
-    k3moe_pack_mxfp4, k3moe_tiled_scale_bytes, pack_mxfp4, pack_layer_weights,
+    k3moe_pack_mxfp4, k3moe_pack_mxfp4_from_host, k3moe_tiled_scale_bytes, pack_mxfp4,
+    pack_mxfp4_from_host, pack_layer_weights, pack_layer_weights_from_host,
 )

@@ -88,6 +88,8 @@ def load_library():
     lib.k3moe_experts_forward.restype = ctypes.c_int
     lib.k3moe_pack_mxfp4.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.k3moe_pack_mxfp4.restype = ctypes.c_int
+    lib.k3moe_pack_mxfp4_from_host.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.k3moe_pack_mxfp4_from_host.restype = ctypes.c_int
     lib.k3moe_tiled_scale_bytes.argtypes = [i32, i32, i32]
     lib.k3moe_tiled_scale_bytes.restype = i64
     lib.k3moe_profile_begin.argtypes = [vp, i32]
@@ -203,6 +205,49 @@ def k3moe_pack_mxfp4(codes, scales, n, R, K, tiled_codes, tiled_scales, stream=N
     rc = load_library().k3moe_pack_mxfp4(_ptr(codes), _ptr(scales), n, R, K, _ptr(tiled_codes),
                                          _ptr(tiled_scales), _stream(stream, codes.device))
     _check(rc, "k3moe_pack_mxfp4")
+
+
+def _host_ptr(a):
+    """Data pointer of a host numpy array or CPU torch tensor (C-contiguous)."""
+    if hasattr(a, "data_ptr"):
+        if a.is_cuda or not a.is_contiguous():
+            raise ValueError("expected a contiguous host tensor")
+        return ctypes.c_void_p(a.data_ptr())
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("expected a C-contiguous host array")
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def k3moe_pack_mxfp4_from_host(codes, scales, n, R, K, tiled_codes, tiled_scales, stream=None):
+    """Row-major host codes/scales (numpy or CPU tensors) -> tiled device tensors."""
+    rc = load_library().k3moe_pack_mxfp4_from_host(_host_ptr(codes), _host_ptr(scales), n, R, K,
+                                                   _ptr(tiled_codes), _ptr(tiled_scales),
+                                                   _stream(stream, tiled_codes.device))
+    _check(rc, "k3moe_pack_mxfp4_from_host")
+
+
+def pack_mxfp4_from_host(codes, scales, n, R, K, device="cuda"):
+    """Row-major host matrices -> new tiled device tensors (flat uint8)."""
+    import torch
+    tc = torch.empty(n * R * K // 2, dtype=torch.uint8, device=device)
+    ts = torch.empty(k3moe_tiled_scale_bytes(n, R, K), dtype=torch.uint8, device=device)
+    k3moe_pack_mxfp4_from_host(codes, scales, n, R, K, tc, ts)
+    return tc, ts
+
+
+def pack_layer_weights_from_host(w: dict, E: int, d: int, f: int, device="cuda") -> dict:
+    """Row-major layer weights in host memory (the six MXFP4 tensors; router_w
+    and router_b as host arrays or None) -> device weights for k3moe_create."""
+    import numpy as np
+    import torch
+    out = {}
+    for name, (R, K) in (("gate", (f, d)), ("up", (f, d)), ("down", (d, f))):
+        out[name + "_q"], out[name + "_s"] = pack_mxfp4_from_host(w[name + "_q"], w[name + "_s"],
+                                                                  E, R, K, device)
+    for name in ("router_w", "router_b"):
+        v = w.get(name)
+        out[name] = None if v is None else torch.as_tensor(np.asarray(v, dtype=np.float32)).to(device)
+    return out
 
 
 def pack_mxfp4(codes, scales, n, R, K):

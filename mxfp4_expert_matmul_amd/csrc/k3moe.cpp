@@ -19,6 +19,8 @@ using k3::Shape;
 namespace {
 
 constexpr size_t kAlign = 256;
+// device staging of k3moe_pack_mxfp4_from_host: row-major matrices per chunk
+constexpr size_t kPackStageBytes = (size_t)32 << 20;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -331,6 +333,52 @@ int k3moe_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int32_t n, int
     if (!aligned(p, 16)) return K3MOE_EINVAL;
   return hip_status(k3::launch_pack(codes, scales, n, R, K, tiled_codes, tiled_scales,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int k3moe_pack_mxfp4_from_host(const uint8_t* codes, const uint8_t* scales, int32_t n, int32_t R,
+                               int32_t K, uint8_t* tiled_codes, uint8_t* tiled_scales,
+                               void* stream) {
+  if (!codes || !scales || !tiled_codes || !tiled_scales) return K3MOE_EINVAL;
+  if (n <= 0 || R <= 0 || K <= 0 || R % 16 != 0 || K % 128 != 0) return K3MOE_EINVAL;
+  if (!aligned(tiled_codes, 16) || !aligned(tiled_scales, 16)) return K3MOE_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t cb = (size_t)R * K / 2, sb = (size_t)R * (K / 32);  // one matrix, row-major
+  const size_t tb = k3::tiled_scale_bytes(1, R, K);                 // its tiled scales
+  // matrices per chunk: as many as fit the staging bytes, at least one
+  const size_t per = align_up(cb) + align_up(sb);
+  const size_t m = std::max<size_t>(1, std::min<size_t>((size_t)n, kPackStageBytes / per));
+  const size_t stage_bytes = align_up(m * cb) + align_up(m * sb);
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+    (void)hipGetLastError();
+    return K3MOE_EHIP;
+  }
+  if (stage_bytes > free_b) return K3MOE_ENOMEM;
+  void* stage = nullptr;
+  if (hipMalloc(&stage, stage_bytes) != hipSuccess || !stage) {
+    (void)hipGetLastError();
+    return K3MOE_ENOMEM;
+  }
+  uint8_t* sc = static_cast<uint8_t*>(stage);
+  uint8_t* ss = sc + align_up(m * cb);
+  // chunk by chunk on one stream: its copy lands after the previous chunk's
+  // pack has read the staging buffer (stream order)
+  hipError_t e = hipSuccess;
+  for (size_t i0 = 0; i0 < (size_t)n && e == hipSuccess; i0 += m) {
+    const size_t cnt = std::min(m, (size_t)n - i0);
+    e = hipMemcpyAsync(sc, codes + i0 * cb, cnt * cb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(ss, scales + i0 * sb, cnt * sb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+      e = k3::launch_pack(sc, ss, (int)cnt, R, K, tiled_codes + i0 * cb, tiled_scales + i0 * tb, st);
+  }
+  const hipError_t es = hipStreamSynchronize(st);  // the staging buffer is free after this
+  (void)hipFree(stage);
+  if (e != hipSuccess || es != hipSuccess) {
+    (void)hipGetLastError();
+    return K3MOE_EHIP;
+  }
+  return K3MOE_OK;
 }
 
 int64_t k3moe_workspace_bytes(const k3moe_config* cfg) {

@@ -40,32 +40,42 @@ def tiled_scale_bytes(n: int, R: int, K: int) -> int:
     return n * (R // 16) * ((K // 128 + 3) // 4) * 256
 
 
-def device_weights(cfg: LayerConfig, device="cuda:0", tiled: bool = True) -> dict:
-    """All layer weights on the device: router_w, router_b (or None) and the
-    six MXFP4 tensors (uint8, flat), generated in place. With tiled=True the
-    codes and scales are in the tiled layout the layer library reads (the
-    same draws, placed by their row-major index); else row-major."""
+def device_tensor(cfg: LayerConfig, name: str, device="cuda:0", tiled: bool = True):
+    """One MXFP4 weight tensor of the layer (gate_q, gate_s, up_q, up_s,
+    down_q or down_s) on the device, uint8, generated in place: in the tiled
+    layout the layer library reads (flat; the same draws placed by their
+    row-major index) or row-major ([E][R][K/2] codes, [E][R][K/32] scales)."""
     import torch
     lib = _load()
     dev = torch.device(device)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     dims = {"gate": (cfg.f, cfg.d), "up": (cfg.f, cfg.d), "down": (cfg.d, cfg.f)}
+    shape = cfg.tensor_shapes()[name]
+    key = stream_key(cfg.seed, WEIGHT_STREAMS[name])
+    R, K = dims[name[:-2]]
+    if tiled:
+        nbytes = int(np.prod(shape)) if name.endswith("_q") else tiled_scale_bytes(cfg.E, R, K)
+        t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        fn = lib.k3synth_fill_codes_tiled if name.endswith("_q") else lib.k3synth_fill_scales_tiled
+        rc = fn(ctypes.c_void_p(t.data_ptr()), cfg.E, R, K, key, stream)
+    else:
+        t = torch.empty(shape, dtype=torch.uint8, device=dev)
+        fn = lib.k3synth_fill_codes if name.endswith("_q") else lib.k3synth_fill_scales
+        rc = fn(ctypes.c_void_p(t.data_ptr()), t.numel(), key, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth fill of {name} failed ({rc})")
+    return t
+
+
+def device_weights(cfg: LayerConfig, device="cuda:0", tiled: bool = True) -> dict:
+    """All layer weights on the device: router_w, router_b (or None) and the
+    six MXFP4 tensors (uint8), generated in place, tiled or row-major as in
+    device_tensor."""
+    import torch
+    dev = torch.device(device)
     out = {}
-    for name, shape in cfg.tensor_shapes().items():
-        key = stream_key(cfg.seed, WEIGHT_STREAMS[name])
-        R, K = dims[name[:-2]]
-        if tiled:
-            nbytes = int(np.prod(shape)) if name.endswith("_q") else tiled_scale_bytes(cfg.E, R, K)
-            t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            fn = lib.k3synth_fill_codes_tiled if name.endswith("_q") else lib.k3synth_fill_scales_tiled
-            rc = fn(ctypes.c_void_p(t.data_ptr()), cfg.E, R, K, key, stream)
-        else:
-            t = torch.empty(shape, dtype=torch.uint8, device=dev)
-            fn = lib.k3synth_fill_codes if name.endswith("_q") else lib.k3synth_fill_scales
-            rc = fn(ctypes.c_void_p(t.data_ptr()), t.numel(), key, stream)
-        if rc != 0:
-            raise RuntimeError(f"synth fill of {name} failed ({rc})")
-        out[name] = t
+    for name in cfg.tensor_shapes():
+        out[name] = device_tensor(cfg, name, dev, tiled)
     out["router_w"] = torch.from_numpy(gen_router_w(cfg)).to(dev)
     b = gen_bias(cfg)
     out["router_b"] = None if b is None else torch.from_numpy(b).to(dev)

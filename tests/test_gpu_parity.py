@@ -131,6 +131,40 @@ def test_pack_matches_layout_definition(k3):
         assert np.array_equal(ts.cpu().numpy(), ws), (n, R, K)
 
 
+def test_pack_from_host_matches_layout_definition(k3):
+    """Row-major matrices in host memory (numpy, and pinned CPU tensors) ->
+    the tiled device layout, against the layout written out from its
+    definition; a shape big enough to take several staging chunks against
+    the device-side pack of the same bytes."""
+    rng = np.random.default_rng(6)
+    for n, R, K in [(2, 32, 128), (1, 48, 640), (3, 16, 512)]:
+        codes = rng.integers(0, 256, (n, R, K // 2), dtype=np.uint8)
+        scales = rng.integers(0, 256, (n, R, K // 32), dtype=np.uint8)
+        wc, ws = _tiled_reference(codes, scales, R, K)
+        for src in ("numpy", "pinned"):
+            c_h, s_h = codes, scales
+            if src == "pinned":
+                c_h = torch.from_numpy(codes).pin_memory()
+                s_h = torch.from_numpy(scales).pin_memory()
+            tc, ts = k3.pack_mxfp4_from_host(c_h, s_h, n, R, K)
+            assert np.array_equal(tc.cpu().numpy(), wc), (n, R, K, src)
+            assert np.array_equal(ts.cpu().numpy(), ws), (n, R, K, src)
+    n, R, K = 40, 1024, 4096  # 2 MB per matrix: three chunks of the 32 MiB staging buffer
+    codes = rng.integers(0, 256, (n, R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (n, R, K // 32), dtype=np.uint8)
+    tc, ts = k3.pack_mxfp4_from_host(codes, scales, n, R, K)
+    dc, ds = k3.pack_mxfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), n, R, K)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, dc) and torch.equal(ts, ds)
+    bad = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(k3.K3MoEError) as ei:  # misaligned destination
+        k3.k3moe_pack_mxfp4_from_host(codes, scales, 1, R, K, bad[1:], bad)
+    assert ei.value.status == k3.K3MOE_EINVAL
+    with pytest.raises(k3.K3MoEError) as ei:  # R not a multiple of 16
+        k3.k3moe_pack_mxfp4_from_host(codes, scales, 1, 15, K, bad, bad)
+    assert ei.value.status == k3.K3MOE_EINVAL
+
+
 def test_device_generator_matches_host(k3):
     from synth.device import device_weights, host_weights_to_device
     cfg = synth.CONFIGS[1]
@@ -642,6 +676,10 @@ def big_layers(k3):
     state = {}
 
     def get(ci, max_tokens):
+        if ci is None:  # release
+            state.clear()
+            torch.cuda.empty_cache()
+            return None
         if state.get("ci") != ci:
             state.clear()
             torch.cuda.empty_cache()
@@ -664,6 +702,53 @@ def test_k3_decode(k3, big_layers):
     cfg = st["cfg"]
     x = synth.gen_x(cfg)
     _run_and_check(k3, st["layer"], cfg, x, st["src"], st["wr"], st["bias"], label="k3 decode")
+
+
+@pytest.mark.timeout(600)
+def test_k3_layer_from_row_major_host_weights(k3, big_layers):
+    """A K3-shape layer loaded the way a checkpoint would be: all six MXFP4
+    tensors (21 GB) row-major in pinned host memory, packed into the tiled
+    device layout through k3moe_pack_mxfp4_from_host (the device then holds
+    the tiled tensors and a staging buffer of at most 32 MiB, never a second
+    full copy). The tiled tensors equal the generator's tiled ones bit for
+    bit, and the layer created from them matches the oracle at decode."""
+    from synth.device import device_tensor
+    big_layers(None, 0)  # release the resident K3 layer first
+    cfg = synth.CONFIGS[2]
+    host = {}
+    for name in cfg.tensor_shapes():
+        t = device_tensor(cfg, name, tiled=False)
+        h = torch.empty(t.shape, dtype=torch.uint8, pin_memory=True)
+        h.copy_(t)
+        host[name] = h
+        del t
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    tiled_bytes = sum(int(np.prod(s)) for n, s in cfg.tensor_shapes().items() if n.endswith("_q"))
+    tiled_bytes += sum(k3.k3moe_tiled_scale_bytes(cfg.E, *rk) for rk in
+                       ((cfg.f, cfg.d), (cfg.f, cfg.d), (cfg.d, cfg.f)))
+    free0 = torch.cuda.mem_get_info()[0]
+    host["router_w"] = synth.gen_router_w(cfg)
+    host["router_b"] = None
+    dw = k3.pack_layer_weights_from_host(host, cfg.E, cfg.d, cfg.f)
+    torch.cuda.synchronize()
+    used = free0 - torch.cuda.mem_get_info()[0]
+    _say(f"[k3 host load] tiled tensors {tiled_bytes / 1e9:.3f} GB; device memory taken {used / 1e9:.3f} GB")
+    assert used < tiled_bytes + (256 << 20)  # the tensors (+ the router), the staging freed again
+    for name in cfg.tensor_shapes():
+        ref = device_tensor(cfg, name, tiled=True)
+        assert torch.equal(dw[name], ref), name
+        del ref
+    del host
+    layer = _layer(k3, cfg, dw, 8)
+    x = synth.gen_x(cfg, T=2)
+    try:
+        _run_and_check(k3, layer, cfg, x, synth.ExpertSource(cfg), synth.gen_router_w(cfg), None,
+                       label="k3 from host row-major")
+    finally:
+        layer.close()
+        del dw
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(600)
