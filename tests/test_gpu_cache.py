@@ -281,3 +281,73 @@ def test_prefetch_refusals(k3):
     assert st["prefetched"] == free + 1
     cached.close()
     full.close()
+
+
+def test_layer_stack_route_ahead_prefetch(k3):
+    """Four layers (each its own seeded weights, 64 experts, top-8) with their
+    experts in host memory behind 24-slot arenas, joined by a residual update
+    (x + 0.25 y at x's RMS, in bf16). While layer l runs, layer l+1's experts
+    are predicted by routing layer l's input through layer l+1's router on a
+    side stream and prefetched on a copy stream (the last layer predicts the
+    next step's layer 0). Every layer's output of every step equals the
+    all-resident stack's bit for bit; prefetched experts are hit, and the true
+    resident hits (hits minus prefetch hits) stay below the raw ones."""
+    import dataclasses
+    from synth.device import host_weights_to_device
+    base = synth.CONFIGS[1]
+    L, T, steps, alpha = 4, 2, 8, 0.25
+    c = k3.Config(base.d, base.E, base.k, base.f, T)
+    full, cached, routers = [], [], []
+    stub = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    for l in range(L):
+        cfg = dataclasses.replace(base, seed=base.seed + 100 * (l + 1))
+        _, _, f_l, c_l = _layers(k3, cfg, T, 40)
+        full.append(f_l)
+        cached.append(c_l)
+        wr = synth.gen_router_w(cfg)
+        routers.append(k3.Layer(c, dict({n: stub for n in EXPERT_TENSORS},
+                                        router_w=torch.from_numpy(wr).cuda(), router_b=None), 0))
+
+    def update(x, y):
+        xf = x.float()
+        rx = xf.pow(2).mean(dim=-1, keepdim=True).sqrt()
+        ry = y.pow(2).mean(dim=-1, keepdim=True).sqrt().clamp_min(1e-30)
+        return (xf + y * (alpha * rx / ry)).to(torch.bfloat16)
+
+    pool = [_xd(x) for x in np.split(synth.gen_x(base, T=T * (steps + 1), stream=22), steps + 1)]
+    ref = []
+    for i in range(steps):
+        x, ys = pool[i], []
+        for l in range(L):
+            y, _, _ = full[l].forward(x)
+            ys.append(y)
+            x = update(x, y)
+        ref.append(ys)
+    torch.cuda.synchronize()
+    route_st, copy_st = torch.cuda.Stream(), torch.cuda.Stream()
+    ridx = torch.empty((T, base.k), dtype=torch.int32, device="cuda")
+    rgate = torch.empty((T, base.k), dtype=torch.float32, device="cuda")
+    out = []
+    for i in range(steps):
+        x, ys = pool[i], []
+        for l in range(L):
+            y, _, _ = cached[l].forward(x)
+            ys.append(y)
+            nl, nx = (l + 1, x) if l + 1 < L else (0, pool[i + 1])
+            with torch.cuda.stream(route_st):
+                route_st.wait_stream(torch.cuda.current_stream())
+                k3.k3moe_route(routers[nl].handle, nx, ridx, rgate, stream=route_st)
+                guess = ridx.cpu().reshape(-1).tolist()
+            cached[nl].prefetch(guess, stream=copy_st)
+            x = update(x, y)
+        out.append(ys)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for l in range(L):
+            assert torch.equal(out[i][l], ref[i][l]), f"step {i} layer {l}: output differs"
+    for l in range(L):
+        st = cached[l].stats()
+        assert st["prefetched"] > 0 and st["prefetch_hits"] > 0, (l, st)
+        assert st["hits"] - st["prefetch_hits"] < st["hits"], (l, st)
+    for obj in full + cached + routers:
+        obj.close()
