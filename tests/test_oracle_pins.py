@@ -222,6 +222,13 @@ def test_selection_only_bias():
         assert np.array_equal(di, idx)
         w = g[0] * np.exp(sel[idx[0]].astype(np.float64) - raw[idx[0]].astype(np.float64))
         assert np.allclose(dgb[0], w / w.sum(), rtol=1e-12, atol=1e-15)
+    # a bias far larger than the logits (selection by bias alone) leaves the
+    # gates the softmax of the raw logits: no term may under- or overflow
+    raw = np.array([0.3, -1.2, 2.0, 0.1, -0.4, 1.1], np.float32)
+    big = np.array([900.0, 0.0, 850.0, -900.0, 880.0, 0.0], np.float32)
+    idx, g = oracle.topk_gates((raw + big)[None, :], 3, gate_logits=raw[None, :])
+    assert list(idx[0]) == [0, 4, 2]
+    assert np.allclose(g[0], softmax(raw[[0, 4, 2]].astype(np.float64)), rtol=1e-14, atol=0)
     cfg = synth.CONFIGS[1]
     bias = synth.skew_bias(4, cfg.E)
     x0 = np.zeros((1, cfg.d), dtype=np.uint16)
