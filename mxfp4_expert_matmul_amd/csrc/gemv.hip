@@ -95,28 +95,30 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-// gate/up: one wave per (pair, 16-row tile of gate and of up). The wave
-// first copies the token's x (bf16) into its own LDS region (buffer loads to
-// LDS), then walks K four 128-column tiles per step with the next
-// kGuDepth - 1 steps' weights in flight (ten buffer loads per step: four
-// 1 KB tiles of gate, four of up, one scale dword of each; past the last
-// tile they read zeros without touching memory). Lane (r, g) takes row
+// gate/up: one wave per (pair, 16-row tile of gate and of up); the four
+// waves of a workgroup serve one pair. With `logits` given (the whole-layer
+// call) each wave first loads its token's logits, then its share of the
+// token's x (bf16) into the workgroup's LDS (buffer loads to LDS, one copy
+// per workgroup), then selects the token's top k itself (the same selection
+// as the top-k kernel, waiting for the logits alone) and takes its pair's
+// expert from it, so no top-k launch sits between the router and this
+// kernel; the workgroup of slot 0 and row block 0 writes the token's idx and
+// gates for the down GEMV and the caller. Otherwise idx is the caller's
+// routing. The wave then walks K four 128-column tiles per step with the
+// next kGuDepth - 1 steps' weights in flight (ten buffer loads per step:
+// four 1 KB tiles of gate, four of up, one scale dword of each; past the
+// last tile they read zeros without touching memory); one barrier before
+// the first step's compute makes the whole x visible. Lane (r, g) takes row
 // 16 rt + r, K block g of every tile, so one 16-byte load per lane reads a
 // whole 1 KB tile; its 32 activations are the same for the 16 lanes of a
 // group (an LDS broadcast). Rows are summed over the 4 groups at the end.
-// With `logits` given (the whole-layer call), each wave first selects its
-// token's top k itself (the same selection as the top-k kernel, no workgroup
-// sync) and takes its pair's expert from it, so no top-k launch sits between
-// the router and this kernel; the workgroup of slot 0 and row block 0
-// writes the token's idx and gates for the down GEMV and the caller.
-// Otherwise idx is the caller's routing.
 // grid: (T*k pairs, ceil(f / 64)), block 256 (4 waves = 4 row tiles),
-// dynamic LDS 4 x XC KB.
+// dynamic LDS (XC + 1) KB.
 constexpr int kGuTiles = 4;
 constexpr int kGuDepth = 3;
 constexpr int kGuLoads = 2 * kGuTiles + 2;
 
-// 1 KB copies of x per wave (d <= 512 XC; lanes past d read zeros)
+// 1 KB pieces of x (d <= 512 XC; bytes past d read as zeros)
 __host__ __device__ constexpr int gu_x_copies(int d) {
   return d <= 1024 ? 2 : d <= 2048 ? 4 : d <= 4096 ? 8 : d <= 7168 ? 14 : 16;
 }
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     const float* __restrict__ logits, const float* __restrict__ sel_bias,
     int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ h32) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [4][512 * XC]
+  extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [512 * XC] + a 1 KB dump
   __shared__ uint64_t cand[4][64];
   __shared__ uint64_t sel[4][64];
   const int lane = threadIdx.x & 63;
@@ -137,24 +139,33 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   const int pair = blockIdx.x;
   const int rt = blockIdx.y * 4 + wave;
   const int RT = f >> 4, KT = d >> 7, KG = (KT + 3) >> 2;
-  if (rt >= RT) return;  // waves work independently (no barrier)
   const int t = pair / k, j = pair - t * k;
-  uint16_t* xw = xl + (size_t)wave * 512 * XC;
-  {  // x first: its copy does not depend on the expert
+  // the token's logits first: the selection then waits for them alone, not
+  // for the x copies issued after them
+  const float* lrow = logits ? logits + (size_t)t * E : nullptr;
+  TopkRow<V> rw;
+  if (logits) topk_load<V>(lrow, E, sel_bias, rw);
+  uint16_t* xw = xl;
+  {  // x once per workgroup (all four waves serve one pair): wave w copies
+     // 1 KB pieces w, w + 4, ...; a piece number past x's end goes to the
+     // dump kilobyte and reads nothing
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(x + (size_t)t * d), 0, 2 * d, 0x00020000);
+    constexpr int kPer = (XC + 3) / 4;
 #pragma unroll
-    for (int v = 0; v < XC; ++v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_ptr)(xw + 512 * v), 16,
-                                               16 * lane + 1024 * v, 0, 0, 0);
+    for (int i = 0; i < kPer; ++i) {
+      const int v = wave + 4 * i;
+      const bool in = v < XC;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_ptr)(xl + 512 * (in ? v : XC)), 16,
+                                               in ? 16 * lane + 1024 * v : (int)0x7fff0000, 0, 0, 0);
+    }
   }
   int e;
   if (logits) {
-    const float* row = logits + (size_t)t * E;
-    const uint64_t mine = topk_token<V>(row, E, k, cand[wave], sel[wave], sel_bias);
+    const uint64_t mine = topk_select<V>(rw, sel_bias != nullptr, E, k, cand[wave], sel[wave]);
     e = ~__builtin_amdgcn_readlane((int)(uint32_t)mine, j);  // selection j's expert
     if (j == 0 && blockIdx.y == 0 && wave == 0) {
-      const float g = sel_bias ? topk_gate_unbiased(mine, k, row) : topk_gate_of(mine, k);
+      const float g = sel_bias ? topk_gate_unbiased(mine, k, lrow) : topk_gate_of(mine, k);
       if (lane < k) {
         idx[(size_t)t * k + lane] = topk_key_index(mine);
         gate[(size_t)t * k + lane] = g;
@@ -162,7 +173,16 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     }
   } else {
     e = idx[pair];
-    if (e < 0 || e >= E) return;  // dropped pair: never read downstream
+    if (e < 0 || e >= E) {  // dropped pair (the whole workgroup): never read downstream
+      gemv_wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
+      return;
+    }
+  }
+  if (rt >= RT) {  // past the last row tile: the copies and the barrier only
+    gemv_wait_vmcnt<0>();
+    gemv_fence();
+    __builtin_amdgcn_s_barrier();
+    return;
   }
   // buffers over this row tile's K tiles (codes) and scale groups
   const size_t row = (size_t)e * RT + rt;
@@ -179,15 +199,19 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     uint32_t sg, su;
   };
   // step s: K tiles 4s .. 4s + 3 and their scale group s (offsets past the
-  // buffers read zeros)
+  // buffers read zeros). The per-lane offsets pass through an asm statement
+  // at the issue point, so no load can be hoisted above it: the compiler does
+  // not order these buffer loads against the fences' memory clobbers.
   auto issue = [&](int s, Ring& b) {
+    int vq = 16 * lane, vs = 4 * lane;
+    asm volatile("" : "+v"(vq), "+v"(vs));
 #pragma unroll
     for (int i = 0; i < kGuTiles; ++i) {
-      b.qg[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, 16 * lane + 1024 * (4 * s + i), 0, kNonTemporal);
-      b.qu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, 16 * lane + 1024 * (4 * s + i), 0, kNonTemporal);
+      b.qg[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, vq + 1024 * (4 * s + i), 0, kNonTemporal);
+      b.qu[i] = __builtin_amdgcn_raw_buffer_load_b128(ru, vq + 1024 * (4 * s + i), 0, kNonTemporal);
     }
-    b.sg = __builtin_amdgcn_raw_buffer_load_b32(rgs, 4 * lane + 256 * s, 0, 0);
-    b.su = __builtin_amdgcn_raw_buffer_load_b32(rus, 4 * lane + 256 * s, 0, 0);
+    b.sg = __builtin_amdgcn_raw_buffer_load_b32(rgs, vs + 256 * s, 0, 0);
+    b.su = __builtin_amdgcn_raw_buffer_load_b32(rus, vs + 256 * s, 0, 0);
   };
   float ga = 0.0f, ua = 0.0f;
   auto compute = [&](int s, const Ring& b) {
@@ -213,7 +237,18 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   // at compile time; steps past the last read zeros and compute nothing
   Ring ring[kGuDepth];
   gemv_fence();
-  static_for<kGuDepth - 1>([&](auto P) { issue(P(), ring[P()]); });
+  static_for<kGuDepth - 1>([&](auto P) {
+    issue(P(), ring[P()]);
+    gemv_fence();  // one step's loads, tiles then scales, before the next step's
+    // A second use of the step's registers in a branch that is never taken
+    // (KT >= 1): with uses in two blocks the compiler cannot sink the loads
+    // into the first compute's bounds branch, after the later steps' loads.
+    if (KT < 0) {
+      const Ring& b = ring[P()];
+      asm volatile("" ::"v"(b.qg[0]), "v"(b.qg[1]), "v"(b.qg[2]), "v"(b.qg[3]), "v"(b.qu[0]),
+                   "v"(b.qu[1]), "v"(b.qu[2]), "v"(b.qu[3]), "v"(b.sg), "v"(b.su));
+    }
+  });
   static_for<XC>([&](auto S) {
     constexpr int s = S();
     gemv_fence();
@@ -223,6 +258,10 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     constexpr int after = (XC - 1 - s < kGuDepth - 1 ? XC - 1 - s : kGuDepth - 1) * kGuLoads;
     gemv_wait_vmcnt<after>();
     gemv_fence();
+    if constexpr (s == 0) {  // every wave's pieces of x have landed
+      __builtin_amdgcn_s_barrier();
+      gemv_fence();
+    }
     if (4 * s < KT) compute(s, ring[s % kGuDepth]);
   });
   gemv_wait_vmcnt<0>();
@@ -396,7 +435,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void gemv_down_kernel(
   }
 }
 
-static size_t gateup_lds_bytes(int d) { return (size_t)4 * 1024 * gu_x_copies(d); }
+static size_t gateup_lds_bytes(int d) { return (size_t)1024 * (gu_x_copies(d) + 1); }
 
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, const Shape& s, const ExpertWeights& w,
                               const float* logits, const float* sel_bias, int32_t* idx,
@@ -470,7 +509,8 @@ hipError_t prepare_gemv_all() {
   hipError_t e = hipSuccess;
   auto gu = [&](const void* fn, int xc) {
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 1024 * xc);
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              1024 * (xc + 1));
   };
 #define K3_GU_ALL(XC)                                                       \
   gu(reinterpret_cast<const void*>(gemv_gateup_kernel<XC, 16>), XC);        \

@@ -123,22 +123,50 @@ __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand,
   return mine;
 }
 
-// Keys of token row `row` (E logits, V per lane), then their top k: lane
-// r < k returns selection r. With sel_bias (the selection-only bias) the
-// keys rank row[e] + sel_bias[e], added in fp32.
+// One token row's logits (E of them, V per lane: lane l holds experts
+// l + 64 j), and the selection-only bias beside them when there is one.
+// Loading is split from selecting so a caller can issue these loads before
+// other loads and wait for these alone.
+template <int V>
+struct TopkRow {
+  float l[V], b[V];
+};
+
 template <int V>  // logits per lane: E <= 64 * V
-__device__ __forceinline__ uint64_t topk_token(const float* row, int E, int k, uint64_t* cand,
-                                               uint64_t* sel, const float* sel_bias = nullptr) {
+__device__ __forceinline__ void topk_load(const float* row, int E, const float* sel_bias,
+                                          TopkRow<V>& rw) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int e = lane + 64 * j;
+    rw.l[j] = e < E ? row[e] : 0.0f;
+    rw.b[j] = (sel_bias && e < E) ? sel_bias[e] : 0.0f;
+  }
+}
+
+// The top k of a loaded row: lane r < k returns selection r. With the
+// selection-only bias the keys rank l[e] + sel_bias[e], added in fp32.
+template <int V>
+__device__ __forceinline__ uint64_t topk_select(const TopkRow<V>& rw, bool biased, int E, int k,
+                                                uint64_t* cand, uint64_t* sel) {
   const int lane = threadIdx.x & 63;
   uint64_t key[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int e = lane + 64 * j;
-    float v = 0.0f;
-    if (e < E) v = sel_bias ? row[e] + sel_bias[e] : row[e];
+    const float v = biased ? rw.l[j] + rw.b[j] : rw.l[j];
     key[j] = (e < E) ? topk_key(v, e) : 0ull;  // 0 is below every real key
   }
   return select_topk<V>(key, k, cand, sel);
+}
+
+// Keys of token row `row`, then their top k (load and select together).
+template <int V>
+__device__ __forceinline__ uint64_t topk_token(const float* row, int E, int k, uint64_t* cand,
+                                               uint64_t* sel, const float* sel_bias = nullptr) {
+  TopkRow<V> rw;
+  topk_load<V>(row, E, sel_bias, rw);
+  return topk_select<V>(rw, sel_bias != nullptr, E, k, cand, sel);
 }
 
 // Gate of lane r < k's selection: exp(l_r - l_0) / sum over the k selected.
