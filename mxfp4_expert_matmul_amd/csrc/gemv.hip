@@ -79,6 +79,11 @@ __device__ __forceinline__ void gemv_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt on the LDS counter only (lgkmcnt(0); vmcnt and expcnt at their
+// "do not wait" values)
+__device__ __forceinline__ void gemv_wait_lds() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+}
 __device__ __forceinline__ void gemv_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
@@ -97,14 +102,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // gate/up: one wave per (pair, 16-row tile of gate and of up); the four
 // waves of a workgroup serve one pair. With `logits` given (the whole-layer
-// call) each wave first loads its token's logits, then its share of the
-// token's x (bf16) into the workgroup's LDS (buffer loads to LDS, one copy
-// per workgroup), then selects the token's top k itself (the same selection
-// as the top-k kernel, waiting for the logits alone) and takes its pair's
-// expert from it, so no top-k launch sits between the router and this
-// kernel; the workgroup of slot 0 and row block 0 writes the token's idx and
-// gates for the down GEMV and the caller. Otherwise idx is the caller's
-// routing. The wave then walks K four 128-column tiles per step with the
+// call) wave 0 first loads its token's logits, every wave then copies its
+// share of the token's x (bf16) into the workgroup's LDS (buffer loads to
+// LDS, one copy per workgroup), and wave 0 selects the token's top k (the
+// same selection as the top-k kernel, waiting for the logits alone) and
+// passes its pair's expert to the other waves through LDS, so no top-k
+// launch sits between the router and this kernel; the workgroup of slot 0
+// and row block 0 writes the token's idx and gates for the down GEMV and the
+// caller. Otherwise idx is the caller's routing. The wave then walks K four 128-column tiles per step with the
 // next kGuDepth - 1 steps' weights in flight (ten buffer loads per step:
 // four 1 KB tiles of gate, four of up, one scale dword of each; past the
 // last tile they read zeros without touching memory); one barrier before
@@ -131,8 +136,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
     int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ h32) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [512 * XC] + a 1 KB dump
-  __shared__ uint64_t cand[4][64];
-  __shared__ uint64_t sel[4][64];
+  __shared__ __attribute__((aligned(16))) uint64_t cand[kTopkCand];
+  __shared__ uint64_t sel[64];
+  __shared__ int pair_expert;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   // for the x copies issued after them
   const float* lrow = logits ? logits + (size_t)t * E : nullptr;
   TopkRow<V> rw;
-  if (logits) topk_load<V>(lrow, E, sel_bias, rw);
+  if (logits && wave == 0) topk_load<V>(lrow, E, sel_bias, rw);
   uint16_t* xw = xl;
   {  // x once per workgroup (all four waves serve one pair): wave w copies
      // 1 KB pieces w, w + 4, ...; a piece number past x's end goes to the
@@ -162,15 +168,24 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
   }
   int e;
   if (logits) {
-    const uint64_t mine = topk_select<V>(rw, sel_bias != nullptr, E, k, cand[wave], sel[wave]);
-    e = ~__builtin_amdgcn_readlane((int)(uint32_t)mine, j);  // selection j's expert
-    if (j == 0 && blockIdx.y == 0 && wave == 0) {
-      const float g = sel_bias ? topk_gate_unbiased(mine, k, lrow) : topk_gate_of(mine, k);
-      if (lane < k) {
-        idx[(size_t)t * k + lane] = topk_key_index(mine);
-        gate[(size_t)t * k + lane] = g;
+    // wave 0 selects for the workgroup (all four waves serve one pair), the
+    // others take the pair's expert from LDS after a barrier
+    if (wave == 0) {
+      const uint64_t mine = topk_select<V>(rw, sel_bias != nullptr, E, k, cand, sel);
+      if (lane == 0) pair_expert = ~__builtin_amdgcn_readlane((int)(uint32_t)mine, j);
+      if (j == 0 && blockIdx.y == 0) {
+        const float g = sel_bias ? topk_gate_unbiased(mine, k, lrow) : topk_gate_of(mine, k);
+        if (lane < k) {
+          idx[(size_t)t * k + lane] = topk_key_index(mine);
+          gate[(size_t)t * k + lane] = g;
+        }
       }
+      gemv_wait_lds();  // the expert is in LDS (the x copies may still be in flight)
     }
+    gemv_fence();
+    __builtin_amdgcn_s_barrier();
+    gemv_fence();
+    e = __builtin_amdgcn_readfirstlane(pair_expert);
   } else {
     e = idx[pair];
     if (e < 0 || e >= E) {  // dropped pair (the whole workgroup): never read downstream

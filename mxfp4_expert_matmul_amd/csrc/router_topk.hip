@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int k, const float* __restrict__ sel_bias,
                                                    int32_t* __restrict__ idx,
                                                    float* __restrict__ gate) {
-  __shared__ uint64_t cand[4][64];
+  __shared__ __attribute__((aligned(16))) uint64_t cand[4][kTopkCand];
   __shared__ uint64_t sel[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;

@@ -61,7 +61,10 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
 // Usually few keys pass; they are compacted into LDS and each one's rank
 // (the number of passing keys above it) is its position. If more than 64
 // pass, k rounds each take the largest key below the previous round's.
-// Lane r < k returns selection r.
+// Lane r < k returns selection r. cand: kTopkCand entries, 16-byte aligned
+// (the ranking reads up to 7 past the last candidate); sel: 64 entries.
+constexpr int kTopkCand = 72;
+
 template <int V>
 __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand, uint64_t* sel) {
   const int lane = threadIdx.x & 63;
@@ -96,12 +99,20 @@ __device__ uint64_t select_topk(const uint64_t (&key)[V], int k, uint64_t* cand,
   }
   if (c <= 64) {
     const uint64_t mine = lane < c ? cand[lane] : 0ull;
-    int rank = 0;  // passing keys above mine, each broadcast from its lane
-    for (int i = 0; i < c; ++i) {
-      const uint64_t o =
-          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), i) << 32) |
-          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, i);
-      rank += o > mine ? 1 : 0;
+    // rank: the passing keys above mine, read eight at a time as LDS
+    // broadcasts (every lane reads the same address); entries past c are
+    // read but not counted
+    int rank = 0;
+    for (int i0 = 0; i0 < c; i0 += 8) {
+      uint64_t o[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *reinterpret_cast<const uint4*>(cand + i0 + 2 * q);
+        o[2 * q] = ((uint64_t)v.y << 32) | v.x;
+        o[2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rank += (i0 + q < c && o[q] > mine) ? 1 : 0;
     }
     if (lane < c && rank < k) sel[rank] = mine;
     return lane < k ? sel[lane] : 0ull;
