@@ -119,6 +119,36 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, int sa, v8i b, int sb, v4f c)
                                                          0, sb);
 }
 
+// ------------------------------------------------------------- pair slots
+// The down GEMM's per-pair outputs wait in HBM for the combine as 24-bit
+// floats: the top 24 bits of the fp32 value (sign, 8-bit exponent, 15
+// mantissa bits), rounded to nearest (ties away from zero); a NaN stays a
+// quiet NaN, and a value that rounds past the largest becomes infinite.
+// Relative error <= 2^-16, three quarters of the fp32 bytes.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f32_to_f24(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 8) | 0x4000u;  // NaN, kept quiet
+  return (u + 0x80u) >> 8;
+}
+__device__ __forceinline__ float f24_to_f32(uint32_t b) { return __uint_as_float(b << 8); }
+
+// four values -> 12 bytes (three dwords, value 0 in the low bytes)
+__device__ __forceinline__ void pack4_f24(const v4f v, uint32_t* w) {
+  const uint32_t a = f32_to_f24(v[0]), b = f32_to_f24(v[1]), c = f32_to_f24(v[2]),
+                 d = f32_to_f24(v[3]);
+  w[0] = a | (b << 24);
+  w[1] = (b >> 8) | (c << 16);
+  w[2] = (c >> 16) | (d << 8);
+}
+__device__ __forceinline__ void unpack4_f24(const uint32_t* w, float* v) {
+  v[0] = f24_to_f32(w[0] & 0xffffffu);
+  v[1] = f24_to_f32((w[0] >> 24) | ((w[1] & 0xffffu) << 8));
+  v[2] = f24_to_f32((w[1] >> 16) | ((w[2] & 0xffu) << 16));
+  v[3] = f24_to_f32(w[2] >> 8);
+}
+
 // ------------------------------------------------------------- grouped GEMM
 // One workgroup = 4 waves = one (tile, row block): up to kTileM = 96 tokens
 // of one expert (a tile of the grouped pairs) times a block of weight rows.
@@ -272,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, int nrb, uint32_t act_bytes, uint8_t* __restrict__ out_hi,
     uint8_t* __restrict__ out_lo, uint8_t* __restrict__ outs_hi, uint8_t* __restrict__ outs_lo,
-    float* __restrict__ slots) {
+    uint8_t* __restrict__ slots) {
   using G = GemmShape<MODE>;
   constexpr int NM = G::NM, NRT = G::NRT;
   constexpr int NCT = kTileM / 16;  // 16-token MFMA column tiles per wave
@@ -506,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   wait_vmcnt<0>();
   if (!wave_on) return;
 
-  if (MODE == kGateUp) {
+  if constexpr (MODE == kGateUp) {
     // h = SiLU(g) * u, split into two E4M3 terms per 32 features (the wave's
     // 32 features are one MX block; lane (r, g) holds features 16 rt + 4 g + i
     // of token column r).
@@ -560,26 +590,52 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       }
     }
   } else {
-    // this pair's expert output, rows w0 + 16 rt + 4 g + q of token column r,
-    // stored in the pair's own slot (no atomics; summed per token later;
-    // streamed past the caches, it is read once by the combine)
+    // this pair's expert output into the pair's own slot (no atomics; summed
+    // per token later; streamed past the caches, it is read once by the
+    // combine), as 24-bit floats: the wave's 64 rows of a pair are 192
+    // contiguous bytes, 64-byte aligned. Lane (r, g) holds rows
+    // 16 rt + 4 g + i of token column r; it packs each block of four rows
+    // into 12 bytes of a private LDS slice (one 192-byte row per column,
+    // padded against bank conflicts), then reads back and stores 16-byte
+    // pieces so that each store writes 64 contiguous bytes of every column.
+    static_assert(NRT == 4, "the slot layout assumes four row tiles per wave");
+    constexpr int kStRow = 192 + 16;  // bytes per column
+    __shared__ __attribute__((aligned(16))) uint32_t st_all[4][16 * kStRow / 4];
+    uint8_t* st = reinterpret_cast<uint8_t*>(st_all[wave]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       if (ct >= nct) continue;
-      const int i = m0 + 16 * ct + r;
-      if (i >= ti.cnt) continue;
-      const int pair = perm[ti.base + ti.row0 + i];
-      float* o = slots + (size_t)pair * nrows + w0 + 4 * g;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        __builtin_nontemporal_store(acc[0][rt][ct], reinterpret_cast<v4f*>(o + 16 * rt));
+      for (int rt = 0; rt < NRT; ++rt) {
+        uint32_t w[3];
+        pack4_f24(acc[0][rt][ct], w);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(st + r * kStRow + 48 * rt + 12 * g);
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
+      }
+      v4u32 piece[3];  // bytes 64 q + 16 g .. + 15 of column r's 192
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        piece[q] = *reinterpret_cast<const v4u32*>(st + r * kStRow + 64 * q + 16 * g);
+      const int i = m0 + 16 * ct + r;
+      if (i < ti.cnt) {
+        const int pair = perm[ti.base + ti.row0 + i];
+        uint8_t* o = slots + ((size_t)pair * nrows + w0) * 3 + 16 * g;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          __builtin_nontemporal_store(piece[q], reinterpret_cast<v4u32*>(o + 64 * q));
+      }
     }
   }
 }
 
 // y[t] = sum_j gate[t,j] * slot[t*k + j], j in order; pairs whose expert is
-// outside [0, E) contribute zero. One thread per 4 outputs.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slots,
+// outside [0, E) contribute zero. One thread per 4 outputs (12 contiguous
+// bytes of a slot, so a wave's loads are contiguous).
+typedef uint32_t v3u32 __attribute__((ext_vector_type(3), aligned(4)));
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict__ slots,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ gate, int T,
                                                       int d, int k, int E, float* __restrict__ y) {
@@ -589,21 +645,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(i / d4), c = (int)(i % d4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // every slot is read (a dropped pair's slot is allocated but unwritten and
-  // its value is replaced by zero, not multiplied), so the loads of several
+  // its values are replaced by zero, not multiplied), so the loads of several
   // slots are in flight together
 #pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
     const bool on = e >= 0 && e < E;
     const float gw = on ? gate[(size_t)t * k + j] : 0.0f;
-    const v4f vv =
-        __builtin_nontemporal_load(reinterpret_cast<const v4f*>(slots + ((size_t)t * k + j) * d) + c);
-    float4 v = make_float4(vv[0], vv[1], vv[2], vv[3]);
-    if (!on) v = make_float4(0.f, 0.f, 0.f, 0.f);
-    acc.x = fmaf(gw, v.x, acc.x);
-    acc.y = fmaf(gw, v.y, acc.y);
-    acc.z = fmaf(gw, v.z, acc.z);
-    acc.w = fmaf(gw, v.w, acc.w);
+    const v3u32 w3 = __builtin_nontemporal_load(
+        reinterpret_cast<const v3u32*>(slots + (((size_t)t * k + j) * d + 4 * (size_t)c) * 3));
+    const uint32_t w[3] = {w3[0], w3[1], w3[2]};
+    float v[4];
+    unpack4_f24(w, v);
+    if (!on) v[0] = v[1] = v[2] = v[3] = 0.0f;
+    acc.x = fmaf(gw, v[0], acc.x);
+    acc.y = fmaf(gw, v[1], acc.y);
+    acc.z = fmaf(gw, v[2], acc.z);
+    acc.w = fmaf(gw, v[3], acc.w);
   }
   reinterpret_cast<float4*>(y)[i] = acc;
 }
@@ -632,7 +690,7 @@ hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, con
 
 hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* offsets,
                             const int32_t* perm, const int32_t* tiles, const int32_t* ntiles,
-                            int max_tiles, const uint8_t* hq, const uint8_t* hs, float* slots,
+                            int max_tiles, const uint8_t* hq, const uint8_t* hs, uint8_t* slots,
                             hipStream_t st) {
   if (T <= 0 || max_tiles <= 0) return hipSuccess;
   const size_t P = (size_t)T * s.k;
@@ -646,7 +704,7 @@ hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* slots, const int32_t* idx, const float* gate, int T,
+hipError_t launch_combine(const uint8_t* slots, const int32_t* idx, const float* gate, int T,
                           const Shape& s, float* y, hipStream_t st) {
   const size_t n = (size_t)T * (s.d / 4);
   if (n == 0) return hipSuccess;

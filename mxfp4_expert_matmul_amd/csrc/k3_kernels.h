@@ -71,9 +71,9 @@ hipError_t launch_gemm_gateup(int T, const Shape& s, const ExpertWeights& w, con
                               uint8_t* hq, uint8_t* hs, hipStream_t st);
 hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const int32_t* offsets,
                             const int32_t* perm, const int32_t* tiles, const int32_t* ntiles,
-                            int max_tiles, const uint8_t* hq, const uint8_t* hs, float* slots,
+                            int max_tiles, const uint8_t* hq, const uint8_t* hs, uint8_t* slots,
                             hipStream_t st);
-hipError_t launch_combine(const float* slots, const int32_t* idx, const float* gate, int T,
+hipError_t launch_combine(const uint8_t* slots, const int32_t* idx, const float* gate, int T,
                           const Shape& s, float* y, hipStream_t st);
 
 }  // namespace k3

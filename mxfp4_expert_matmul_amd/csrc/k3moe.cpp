@@ -85,7 +85,7 @@ Plan make_plan(const k3moe_config* c) {
   p.hq = take(2 * P * f);
   p.hs = take(2 * P * (f / 32));
   p.h32 = take(tg * k * f * 4);
-  p.slots = take(P * d * 4);
+  p.slots = take(P * d * 3);  // 24-bit floats
   p.wr3 = take(3 * E * d * 2);
   p.total = o;
   p.max_tiles = (int)tiles;
@@ -128,7 +128,7 @@ struct k3moe {
   uint8_t* hq;
   uint8_t* hs;
   float* h32;  // decode: SwiGLU output per pair
-  float* slots;
+  uint8_t* slots;
   uint16_t* wr3;  // router weights as three bf16 terms, derived at create
   // stage timing (k3moe_profile_begin / k3moe_profile_end)
   bool prof_on;
@@ -432,7 +432,7 @@ int k3moe_create(const k3moe_config* cfg, const k3moe_weights* w, int device, k3
   h->hq = h->ws + plan.hq;
   h->hs = h->ws + plan.hs;
   h->h32 = reinterpret_cast<float*>(h->ws + plan.h32);
-  h->slots = reinterpret_cast<float*>(h->ws + plan.slots);
+  h->slots = h->ws + plan.slots;
   h->wr3 = reinterpret_cast<uint16_t*>(h->ws + plan.wr3);
   if (k3::prepare_gemv(shape_of(h)) != hipSuccess ||
       k3::launch_router_split(w->router_w, cfg->n_experts, cfg->d_model, h->wr3, nullptr) !=
