@@ -39,7 +39,8 @@ def test_prefill_bytes_and_flops():
     split_x = 2 * T * cfg.d + 2 * T * (cfg.d // 32)  # two E4M3 terms + their scales
     split_h = 2 * P * cfg.f + 2 * P * (cfg.f // 32)  # two E4M3 terms + their scales
     assert bench.algorithmic_bytes(cfg, T, 896, "gateup") == w + split_x + split_h
-    assert bench.algorithmic_bytes(cfg, T, 896, "combine") == P * cfg.d * 4 + P * 8 + T * cfg.d * 4
+    # combine: the pair slots (24-bit floats) and the routing in, y (fp32) out
+    assert bench.algorithmic_bytes(cfg, T, 896, "combine") == P * cfg.d * 3 + P * 8 + T * cfg.d * 4
     # router at T=4096: 2*T*E*d flops; experts: 3 matrices of 2*d*f per pair
     flops = bench.useful_flops(cfg, T)
     assert flops == pytest.approx(2.0 * P * 3 * cfg.d * cfg.f + 2.0 * T * cfg.d * cfg.E)
