@@ -595,11 +595,16 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     // combine), as 24-bit floats: the wave's 64 rows of a pair are 192
     // contiguous bytes, 64-byte aligned. Lane (r, g) holds rows
     // 16 rt + 4 g + i of token column r; it packs each block of four rows
-    // into 12 bytes of a private LDS slice (one 192-byte row per column,
-    // padded against bank conflicts), then reads back and stores 16-byte
-    // pieces so that each store writes 64 contiguous bytes of every column.
+    // into 12 bytes of a private LDS slice (one 192-byte row per column),
+    // then reads back and stores 16-byte pieces so that each store writes 64
+    // contiguous bytes of every column.
+    // LDS banks: a column's row starts at dword 52 r + 2 (r / 8), so the 32
+    // lanes (r, g < 2) of a half-wave's dword writes (dword 52 r + 3 g + ...
+    // modulo 32 banks) hit 32 distinct banks; without the 2-dword shift
+    // columns r and r + 8 would share banks. The shift leaves rows 8-byte
+    // aligned, so they are read back in 8-byte halves.
     static_assert(NRT == 4, "the slot layout assumes four row tiles per wave");
-    constexpr int kStRow = 192 + 16;  // bytes per column
+    constexpr int kStRow = 192 + 16;  // bytes per column (room for the shift)
     __shared__ __attribute__((aligned(16))) uint32_t st_all[4][16 * kStRow / 4];
     uint8_t* st = reinterpret_cast<uint8_t*>(st_all[wave]);
 #pragma unroll
@@ -609,15 +614,19 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       for (int rt = 0; rt < NRT; ++rt) {
         uint32_t w[3];
         pack4_f24(acc[0][rt][ct], w);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(st + r * kStRow + 48 * rt + 12 * g);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(st + r * kStRow + 8 * (r >> 3) + 48 * rt + 12 * g);
         dst[0] = w[0];
         dst[1] = w[1];
         dst[2] = w[2];
       }
       v4u32 piece[3];  // bytes 64 q + 16 g .. + 15 of column r's 192
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
-        piece[q] = *reinterpret_cast<const v4u32*>(st + r * kStRow + 64 * q + 16 * g);
+      for (int q = 0; q < 3; ++q) {
+        const uint8_t* src = st + r * kStRow + 8 * (r >> 3) + 64 * q + 16 * g;
+        const uint2 a = *reinterpret_cast<const uint2*>(src);
+        const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+        piece[q] = (v4u32){a.x, a.y, b.x, b.y};
+      }
       const int i = m0 + 16 * ct + r;
       if (i < ti.cnt) {
         const int pair = perm[ti.base + ti.row0 + i];
