@@ -325,6 +325,48 @@ int k3moe_cache_prefetch_stats(const k3moe_cache* c, int64_t* prefetched, int64_
  * NULL-safe; never frees the weights. */
 void k3moe_cache_destroy(k3moe_cache* c);
 
+/* Device-planned cache: k3moe_cache_create_ex with flags =
+ * K3MOE_CACHE_DEVICE_PLAN keeps the residency tables in device memory. A
+ * forward then routes, plans (one workgroup, the same replacement rule and
+ * counts as above, call for call), copies the missing experts from the host
+ * tensors with a kernel that reads them over PCIe, and runs the expert
+ * kernels, all enqueued on the call's stream with nothing read back: the call
+ * returns at once, the host never waits, and forwards and device prefetches
+ * can be captured into a HIP graph and replayed (each replay plans anew
+ * against the tables as they then are). The tables and the arena are the
+ * same ones a replay and an eager call use, so graphs and eager calls on one
+ * cache must be ordered by the caller.
+ *   Requirements: the six host tensors are pinned host memory (allocated with
+ *   hipHostMalloc, or torch pin_memory), 16-byte aligned; else K3MOE_EINVAL.
+ *   A forward must have T * top_k <= n_slots (so its distinct experts always
+ *   fit), else K3MOE_EUNSUPPORTED before anything is enqueued.
+ *   k3moe_cache_prefetch (host list) is K3MOE_EINVAL on such a cache; use
+ *   k3moe_cache_prefetch_device. k3moe_cache_stats and
+ *   k3moe_cache_prefetch_stats synchronise the device and read the device
+ *   counters (bytes_in = (misses + prefetched) * one expert's bytes).
+ *   flags = 0 gives the host-planned cache of k3moe_cache_create. */
+#define K3MOE_CACHE_DEVICE_PLAN 1u
+int k3moe_cache_create_ex(const k3moe_config* cfg, const k3moe_host_weights* w, int32_t n_slots,
+                          int device, uint32_t flags, k3moe_cache** out);
+
+/* Prefetch on a device-planned cache: experts is a DEVICE array of n int32
+ * expert ids (for instance the routing of the next call, computed on the
+ * device), read when the plan kernel runs; ids outside [0, E) are skipped and
+ * counted. The same slot rule as k3moe_cache_prefetch; when too few slots
+ * are eligible the prefetch is refused on the device (counted, nothing
+ * changed). The next forward waits for its copies. Errors: K3MOE_EINVAL for a
+ * NULL or host-planned cache, n < 0, or a NULL or misaligned list with n > 0;
+ * K3MOE_EHIP if a launch fails (the cache then forgets every resident
+ * expert). */
+int k3moe_cache_prefetch_device(k3moe_cache* c, const int32_t* experts, int32_t n, void* stream);
+
+/* Counters only a device-planned cache has (HOST outputs, any may be NULL):
+ * prefetches refused for want of eligible slots, and prefetch ids skipped
+ * for lying outside [0, E). Synchronises the device. K3MOE_EINVAL for a NULL
+ * or host-planned cache. */
+int k3moe_cache_device_counters(const k3moe_cache* c, int64_t* refused_prefetches,
+                                int64_t* ignored_ids);
+
 /* Stage timing, a profiling aid. Between k3moe_profile_begin and
  * k3moe_profile_end every forward records a HIP event before and after each
  * stage's kernel launch(es) on the call's own stream, for at most max_calls

@@ -8,7 +8,7 @@ raises instead of falling back to anything else.
 """
 from ._binding import (  # noqa: F401
     K3MOE_OK, K3MOE_EINVAL, K3MOE_ENOMEM, K3MOE_EHIP, K3MOE_EUNSUPPORTED,
-    K3MOE_FLAG_BIAS_SELECT_ONLY,
+    K3MOE_FLAG_BIAS_SELECT_ONLY, K3MOE_CACHE_DEVICE_PLAN,
     K3MoEError, Config, Layer, CachedLayer, load_library, library_path,
     k3moe_create, k3moe_destroy, k3moe_status_str, k3moe_workspace_bytes,
     k3moe_layer_forward, k3moe_layer_forward_noalloc, k3moe_route, k3moe_group, k3moe_experts_forward,

@@ -18,6 +18,7 @@ K3MOE_ENOMEM = -2
 K3MOE_EHIP = -3
 K3MOE_EUNSUPPORTED = -4
 K3MOE_FLAG_BIAS_SELECT_ONLY = 1  # k3moe_config.flags: the router bias only ranks the experts
+K3MOE_CACHE_DEVICE_PLAN = 1  # k3moe_cache_create_ex flags: residency tables and planning on the device
 
 
 class K3MoEError(RuntimeError):
@@ -112,6 +113,13 @@ def load_library():
     lib.k3moe_layer_forward_noalloc.restype = ctypes.c_int
     lib.k3moe_cache_prefetch_stats.argtypes = [vp, vp, vp]
     lib.k3moe_cache_prefetch_stats.restype = ctypes.c_int
+    lib.k3moe_cache_create_ex.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32,
+                                          ctypes.c_int, ctypes.c_uint32, ctypes.POINTER(vp)]
+    lib.k3moe_cache_create_ex.restype = ctypes.c_int
+    lib.k3moe_cache_prefetch_device.argtypes = [vp, vp, i32, vp]
+    lib.k3moe_cache_prefetch_device.restype = ctypes.c_int
+    lib.k3moe_cache_device_counters.argtypes = [vp, vp, vp]
+    lib.k3moe_cache_device_counters.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -306,16 +314,20 @@ class CachedLayer:
     device tensors, the six expert tensors as host (CPU, ideally pinned)
     tensors in the tiled layout. All are borrowed: keep them alive."""
 
-    def __init__(self, cfg: Config, host_weights: dict, n_slots: int, device: int = 0):
+    def __init__(self, cfg: Config, host_weights: dict, n_slots: int, device: int = 0,
+                 device_plan: bool = False):
         lib = load_library()
         self.cfg = cfg
         self._weights = host_weights
+        self.device_plan = bool(device_plan)
         c = cfg._c()
         w = _Weights(*[host_weights.get(n).data_ptr() if host_weights.get(n) is not None else None
                        for n, _ in _Weights._fields_])
         out = ctypes.c_void_p()
-        _check(lib.k3moe_cache_create(ctypes.byref(c), ctypes.byref(w), int(n_slots), int(device),
-                                      ctypes.byref(out)), "k3moe_cache_create")
+        flags = K3MOE_CACHE_DEVICE_PLAN if device_plan else 0
+        _check(lib.k3moe_cache_create_ex(ctypes.byref(c), ctypes.byref(w), int(n_slots),
+                                         int(device), flags, ctypes.byref(out)),
+               "k3moe_cache_create_ex")
         self.handle = out
 
     def forward(self, x, stream=None):
@@ -340,6 +352,22 @@ class CachedLayer:
         _check(load_library().k3moe_cache_prefetch(self.handle, ids, len(experts),
                                                    _stream(stream, torch.device("cuda", device))),
                "k3moe_cache_prefetch")
+
+    def prefetch_device(self, experts, stream=None):
+        """Device-planned caches: prefetch the experts listed in `experts`, a
+        contiguous int32 tensor on the GPU (read when the plan runs), on
+        `stream` (torch stream or None for the current one)."""
+        n = experts.numel()
+        _check(load_library().k3moe_cache_prefetch_device(
+            self.handle, _ptr(experts) if n else None, n, _stream(stream, experts.device)),
+            "k3moe_cache_prefetch_device")
+
+    def device_counters(self) -> dict:
+        """Device-planned caches: refused prefetches and skipped prefetch ids."""
+        v = [ctypes.c_int64() for _ in range(2)]
+        _check(load_library().k3moe_cache_device_counters(self.handle, *[ctypes.byref(a) for a in v]),
+               "k3moe_cache_device_counters")
+        return {"refused_prefetches": v[0].value, "ignored_ids": v[1].value}
 
     def stats(self) -> dict:
         """calls, hits (raw: including experts a prefetch brought in), misses,

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "k3moe")
 LIB = os.path.join(PKG, "libk3moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["layout.hip", "router_topk.hip", "group.hip", "gemv.hip", "gemm.hip", "k3moe.cpp",
-           "cache.cpp"]
+SOURCES = ["layout.hip", "router_topk.hip", "group.hip", "gemv.hip", "gemm.hip", "cache_plan.hip",
+           "k3moe.cpp", "cache.cpp"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

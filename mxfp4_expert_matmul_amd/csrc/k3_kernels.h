@@ -76,4 +76,49 @@ hipError_t launch_gemm_down(int T, const Shape& s, const ExpertWeights& w, const
 hipError_t launch_combine(const uint8_t* slots, const int32_t* idx, const float* gate, int T,
                           const Shape& s, float* y, hipStream_t st);
 
+// cache_plan.hip (device-planned expert cache)
+// Residency tables of an HBM arena of S expert slots for E experts, in device
+// memory; the same fields as the host planner's (lru.h).
+enum CacheCounter : int {
+  kCtrStamp,      // counts every planned forward and prefetch
+  kCtrLastFwd,    // stamp of the last planned forward (0: none)
+  kCtrCalls,      // planned forwards
+  kCtrHits,       // distinct experts found resident (raw: prefetched ones included)
+  kCtrMisses,     // distinct experts copied in by forwards
+  kCtrPfHits,     // hits on experts a prefetch brought in and no forward had used
+  kCtrPrefetched, // experts copied in by prefetches
+  kCtrPfRefused,  // prefetches refused for want of eligible slots
+  kCtrIgnored,    // prefetch ids outside [0, E), skipped
+  kCacheCounters = 16
+};
+struct CacheTables {
+  int32_t* slot_of;     // [E] slot holding expert e, or -1
+  int32_t* expert_in;   // [S] expert in slot s, or -1
+  int64_t* last_use;    // [S] stamp of the last call that used slot s (0: never)
+  int64_t* fwd_use;     // [S] stamp of the last forward that used slot s
+  int32_t* pre;         // [S] 1: brought in by a prefetch, not used by a forward since
+  int64_t* ctr;         // [kCacheCounters]
+  int32_t* fwd_copies;  // [1 + 2 S] the last forward plan's copies: count, (expert, slot)...
+  int32_t* pf_copies;   // [1 + 2 S] the last prefetch plan's copies
+};
+constexpr int kCacheTensors = 6;  // gate codes, gate scales, up codes, up scales, down codes, down scales
+constexpr int kFillChunk = 65536;  // bytes of one expert per fill work item
+constexpr int kFillGrid = 1024;    // fill workgroups (they stride over the work items)
+struct FillPlan {
+  const uint8_t* src[kCacheTensors];  // device-visible pointers to the pinned host tensors
+  uint8_t* dst[kCacheTensors];        // the arena's tensors
+  uint64_t bytes[kCacheTensors];      // one expert's bytes of each tensor (multiples of 256)
+  uint64_t total;                     // their sum
+};
+size_t cache_plan_forward_lds(int P, int E, int S);
+size_t cache_plan_prefetch_lds(int E, int S);
+// once per cache: raise the dynamic LDS limits of the two plan kernels
+hipError_t prepare_cache_plan(int P, int E, int S);
+hipError_t launch_cache_plan_forward(const int32_t* idx, int P, int E, int S, const CacheTables& tb,
+                                     int32_t* sidx, hipStream_t st);
+hipError_t launch_cache_plan_prefetch(const int32_t* experts, int n, int E, int S,
+                                      const CacheTables& tb, hipStream_t st);
+hipError_t launch_cache_fill(const int32_t* copies, int max_copies, int E, int S,
+                             const FillPlan& fp, hipStream_t st);
+
 }  // namespace k3

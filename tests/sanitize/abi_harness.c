@@ -129,6 +129,12 @@ int main(void)
     CHECK(k3moe_cache_forward(NULL, p, 1, (float *)p, NULL, NULL, NULL) == K3MOE_EINVAL, "cache forward NULL");
     int32_t ids[2] = {0, 1};
     CHECK(k3moe_cache_prefetch(NULL, ids, 2, NULL) == K3MOE_EINVAL, "prefetch NULL");
+    CHECK(k3moe_cache_create_ex(&good, &hw, 16, 0, 2u, &c) == K3MOE_EINVAL && c == NULL,
+          "cache unknown flags");
+    CHECK(k3moe_cache_create_ex(&good, NULL, 16, 0, K3MOE_CACHE_DEVICE_PLAN, &c) == K3MOE_EINVAL,
+          "device-planned cache weights NULL");
+    CHECK(k3moe_cache_prefetch_device(NULL, ids, 2, NULL) == K3MOE_EINVAL, "device prefetch NULL");
+    CHECK(k3moe_cache_device_counters(NULL, &a, &b2) == K3MOE_EINVAL, "device counters NULL");
     k3moe_cache_destroy(NULL);
 
     if (g_fail) {

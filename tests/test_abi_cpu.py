@@ -97,6 +97,15 @@ def test_cache_create_validates_before_any_device_call(lib):
     assert out.value is None
     assert dll.k3moe_cache_stats(None, None, None, None, None) == lib.K3MOE_EINVAL
     dll.k3moe_cache_destroy(None)  # NULL-safe
+    # the device-planned variant: unknown flags, and its two entry points on NULL
+    for flags in (2, 3, 0x80000000):
+        assert dll.k3moe_cache_create_ex(C.byref(good), C.byref(w), 16, 0, flags,
+                                         C.byref(out)) == lib.K3MOE_EINVAL
+    assert dll.k3moe_cache_create_ex(C.byref(good), None, 16, 0, lib.K3MOE_CACHE_DEVICE_PLAN,
+                                     C.byref(out)) == lib.K3MOE_EINVAL
+    assert out.value is None
+    assert dll.k3moe_cache_prefetch_device(None, p, 2, None) == lib.K3MOE_EINVAL
+    assert dll.k3moe_cache_device_counters(None, None, None) == lib.K3MOE_EINVAL
 
 
 def test_noalloc_validates_before_any_device_call(lib):
