@@ -16,6 +16,7 @@ namespace {
 
 constexpr int kPlanThreads = 256;
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
 
 // Items i < n with pred(i), compacted in index order: emit(pos, i) for each;
 // returns their count on every thread. wsum: 4 ints of LDS.
@@ -41,24 +42,37 @@ __device__ int compact_in_order(int n, Pred pred, Emit emit, int* wsum) {
   return base;
 }
 
-// Victims: slot s with elig(s) is victim r when r eligible slots come before
-// it in the order (last use ascending, slot ascending), for r < want. The
-// first `want` victims are then exactly the slots the host planner's
-// repeated least-recently-used choice takes, in its order.
-// (The callers guarantee at least `want` eligible slots; entries left -1 by
-// inconsistent tables are skipped by the placement.)
-template <class Elig>
-__device__ void rank_victims(const int64_t* lu, int S, int want, Elig elig, int32_t* vict) {
+// Victim keys: key[s] = (last use << 13) | s for a slot that may take an
+// expert, all ones for the others and for the padding entries S .. S8 - 1
+// (S8 = S rounded up to 8; S < 2^13 and stamps < 2^50). Eligible keys are
+// distinct and order the slots by (last use, slot).
+__device__ __forceinline__ int round8(int n) { return (n + 7) & ~7; }
+__device__ __forceinline__ uint64_t victim_key(bool eligible, int64_t last_use, int s) {
+  return eligible ? (((uint64_t)last_use << 13) | (uint64_t)s) : ~0ull;
+}
+
+// Slot s is victim r when r eligible keys are smaller than its key, for
+// r < want: the first `want` victims are then exactly the slots the host
+// planner's repeated least-recently-used choice takes, in its order. Keys
+// are read two per 16-byte load, and a slot stops counting once its rank
+// reaches `want`. (The callers guarantee at least `want` eligible slots;
+// entries left -1 by inconsistent tables are skipped by the placement.)
+__device__ void rank_victims(const uint64_t* key, int S, int want, int32_t* vict) {
   if (want <= 0) return;
   for (int r = threadIdx.x; r < want; r += kPlanThreads) vict[r] = -1;
   __syncthreads();
+  const int S8 = round8(S);
   for (int s = threadIdx.x; s < S; s += kPlanThreads) {
-    if (!elig(s)) continue;
-    const int64_t ls = lu[s];
+    const uint64_t ks = key[s];
+    if (ks == ~0ull) continue;
     int r = 0;
-    for (int q = 0; q < S; ++q) {
-      const int64_t lq = lu[q];
-      r += (elig(q) && (lq < ls || (lq == ls && q < s))) ? 1 : 0;
+    for (int q = 0; q < S8 && r < want; q += 8) {
+      const v2u64 a = *reinterpret_cast<const v2u64*>(key + q);
+      const v2u64 b = *reinterpret_cast<const v2u64*>(key + q + 2);
+      const v2u64 c = *reinterpret_cast<const v2u64*>(key + q + 4);
+      const v2u64 d = *reinterpret_cast<const v2u64*>(key + q + 6);
+      r += (a.x < ks) + (a.y < ks) + (b.x < ks) + (b.y < ks) + (c.x < ks) + (c.y < ks) +
+           (d.x < ks) + (d.y < ks);
     }
     if (r < want) vict[r] = s;
   }
@@ -89,7 +103,8 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
     const int32_t* __restrict__ idx, int P, int E, int S, CacheTables tb,
     int32_t* __restrict__ sidx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t plan_lds[];
-  int64_t* lu = reinterpret_cast<int64_t*>(plan_lds);  // [S] last use
+  uint64_t* key = reinterpret_cast<uint64_t*>(plan_lds);  // [S8] victim keys
+  int64_t* lu = reinterpret_cast<int64_t*>(key + round8(S));  // [S] last use
   int32_t* first = reinterpret_cast<int32_t*>(lu + S);  // [E] first position in the selection
   int32_t* sel = first + E;                              // [P] the selection
   int32_t* uniq = sel + P;                               // [P] distinct experts
@@ -131,7 +146,12 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
   const int nm = compact_in_order(
       nu, [&](int i) { return tb.slot_of[uniq[i]] < 0; },
       [&](int pos, int i) { missv[pos] = uniq[i]; }, wsum);
-  rank_victims(lu, S, nm, [&](int s) { return lu[s] < call; }, vict);
+  if (nm > 0) {
+    for (int s = tid; s < round8(S); s += kPlanThreads)
+      key[s] = victim_key(s < S && lu[s] < call, s < S ? lu[s] : 0, s);
+    __syncthreads();
+  }
+  rank_victims(key, S, nm, vict);
   __syncthreads();
   for (int j = tid; j < nm; j += kPlanThreads) {
     const int v = vict[j], e = missv[j];
@@ -172,7 +192,8 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
 __global__ __launch_bounds__(kPlanThreads) void cache_plan_prefetch_kernel(
     const int32_t* __restrict__ experts, int n, int E, int S, CacheTables tb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t plan_lds[];
-  int64_t* lu = reinterpret_cast<int64_t*>(plan_lds);  // [S]
+  uint64_t* key = reinterpret_cast<uint64_t*>(plan_lds);  // [S8] victim keys
+  int64_t* lu = reinterpret_cast<int64_t*>(key + round8(S));  // [S]
   int32_t* first = reinterpret_cast<int32_t*>(lu + S);  // [E]
   int32_t* uniq = first + E;                             // [E] distinct listed experts
   int32_t* newv = uniq + E;                              // [E] those not resident
@@ -189,10 +210,16 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_prefetch_kernel(
   }
   __syncthreads();
   const int64_t pst = s_pst, last_fwd = tb.ctr[kCtrLastFwd];
-  for (int s = tid; s < S; s += kPlanThreads) {
-    lu[s] = tb.last_use[s];
-    elig[s] = ((last_fwd == 0 || tb.fwd_use[s] != last_fwd) && lu[s] < pst) ? 1 : 0;
-    if (elig[s]) atomicAdd(&s_free, 1);
+  for (int s0 = 0; s0 < S; s0 += kPlanThreads) {
+    const int s = s0 + tid;
+    bool e = false;
+    if (s < S) {
+      lu[s] = tb.last_use[s];
+      e = (last_fwd == 0 || tb.fwd_use[s] != last_fwd) && lu[s] < pst;
+      elig[s] = e ? 1 : 0;
+    }
+    const uint64_t bal = __ballot(e);
+    if ((tid & 63) == 0 && bal) atomicAdd(&s_free, (int)__builtin_popcountll(bal));
   }
   for (int e = tid; e < E; e += kPlanThreads) first[e] = INT_MAX;
   __syncthreads();
@@ -231,7 +258,12 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_prefetch_kernel(
     }
   }
   __syncthreads();
-  rank_victims(lu, S, nn, [&](int s) { return elig[s] != 0; }, vict);
+  if (nn > 0) {
+    for (int s = tid; s < round8(S); s += kPlanThreads)
+      key[s] = victim_key(s < S && elig[s] != 0, s < S ? lu[s] : 0, s);
+    __syncthreads();
+  }
+  rank_victims(key, S, nn, vict);
   __syncthreads();
   for (int j = tid; j < nn; j += kPlanThreads) {
     const int v = vict[j], e = newv[j];
@@ -275,16 +307,29 @@ __global__ __launch_bounds__(kPlanThreads) void cache_fill_kernel(const int32_t*
             reinterpret_cast<const v4u*>(fp.src[t] + (uint64_t)e * fp.bytes[t] + (b0 - base));
         v4u* dst = reinterpret_cast<v4u*>(fp.dst[t] + (uint64_t)s * fp.bytes[t] + (b0 - base));
         const int nv = (int)((b1 - b0) >> 4);
-#pragma unroll 4
-        for (int i = threadIdx.x; i < nv; i += kPlanThreads) dst[i] = src[i];
+        // eight 16-byte loads in flight per thread before their stores
+        int i = threadIdx.x;
+        for (; i + 7 * kPlanThreads < nv; i += 8 * kPlanThreads) {
+          v4u r[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r[u] = src[i + u * kPlanThreads];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) dst[i + u * kPlanThreads] = r[u];
+        }
+        for (; i < nv; i += kPlanThreads) dst[i] = src[i];
       }
       base += fp.bytes[t];
     }
   }
 }
 
-size_t cache_plan_forward_lds(int P, int E, int S) { return (size_t)S * 8 + (size_t)E * 4 + (size_t)P * 16; }
-size_t cache_plan_prefetch_lds(int E, int S) { return (size_t)S * 13 + (size_t)E * 12; }
+// dynamic LDS of the plan kernels (the layouts at the top of each)
+size_t cache_plan_forward_lds(int P, int E, int S) {
+  return (size_t)((S + 7) & ~7) * 8 + (size_t)S * 8 + (size_t)E * 4 + (size_t)P * 16;
+}
+size_t cache_plan_prefetch_lds(int E, int S) {
+  return (size_t)((S + 7) & ~7) * 8 + (size_t)S * 13 + (size_t)E * 12;
+}
 
 hipError_t prepare_cache_plan(int P, int E, int S) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(cache_plan_forward_kernel),

@@ -103,7 +103,10 @@ struct CacheTables {
 };
 constexpr int kCacheTensors = 6;  // gate codes, gate scales, up codes, up scales, down codes, down scales
 constexpr int kFillChunk = 65536;  // bytes of one expert per fill work item
-constexpr int kFillGrid = 1024;    // fill workgroups (they stride over the work items)
+// fill workgroups: they stride over the work items; 64 keep about 2 MB of
+// PCIe reads in flight, which the link needs, and leave the other CUs to the
+// expert kernels a prefetch overlaps
+constexpr int kFillGrid = 64;
 struct FillPlan {
   const uint8_t* src[kCacheTensors];  // device-visible pointers to the pinned host tensors
   uint8_t* dst[kCacheTensors];        // the arena's tensors
