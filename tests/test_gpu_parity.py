@@ -417,6 +417,94 @@ def test_zero_codes_give_zero(k3, code_byte):
     layer.close()
 
 
+DEQ = synth.LayerConfig("dequant_d256_e2_k1_f256", 256, 2, 1, 256, 8, 5)
+
+
+def _one_weight_matrices(test, i0):
+    """Expert 0's weights for a one-hot x at column i0 (expert 1 all zero),
+    testing one matrix's MXFP4 decode. Row n of the tested matrix holds code
+    n % 16 (all 16 E2M1 codes, twice per 32 rows) at its one non-zero
+    element, with scale byte base + n // 32 for that element's block.
+      gate: g[n] = dq(n), u[n] = 1, down = identity -> y[n] = SiLU(dq(n));
+      up:   g[n] = 96 (SiLU(96) = 96 in fp32), u[n] = dq(n), down = identity
+            -> y[n] = 96 dq(n), exact in fp32;
+      down: h[n] = 96, down row m holds dq(m) at column m -> y[m] = 96 dq(m).
+    Returns the weights and the reference y (float64)."""
+    cfg = DEQ
+    d, f = cfg.d, cfg.f
+    W = {"gate_q": np.zeros((2, f, d // 2), np.uint8), "up_q": np.zeros((2, f, d // 2), np.uint8),
+         "down_q": np.zeros((2, d, f // 2), np.uint8),
+         "gate_s": np.full((2, f, d // 32), 127, np.uint8), "up_s": np.full((2, f, d // 32), 127, np.uint8),
+         "down_s": np.full((2, d, f // 32), 127, np.uint8)}
+    base = {"gate": 128, "up": 120, "down": 112}[test]
+    n = np.arange(f)
+    codes, sbytes = n % 16, base + n // 32
+    dq = np.array([oracle.e2m1_value(int(c)) * oracle.e8m0_value(int(b)) for c, b in zip(codes, sbytes)])
+
+    def put(name, rows, col, code, sbyte):  # element (row, col) of matrix `name` of expert 0
+        q, sc = W[name + "_q"], W[name + "_s"]
+        rows, col = np.broadcast_arrays(rows, col)
+        code = np.broadcast_to(np.asarray(code, np.uint8), rows.shape)
+        byte = q[0, rows, col // 2]
+        # low nibble = even element, high nibble = odd element
+        q[0, rows, col // 2] = np.where(col % 2 == 0, (byte & 0xF0) | code, (byte & 0x0F) | (code << 4))
+        sc[0, rows, col // 32] = sbyte
+
+    if test == "gate":
+        put("gate", n, i0, codes, sbytes)
+        put("up", n, i0, 2, 127)          # 1.0
+        put("down", n, n, 2, 127)         # identity
+        with np.errstate(over="ignore"):  # exp(-dq) = inf for large negative dq: SiLU -> -0
+            ref = dq / (1.0 + np.exp(-dq))
+    elif test == "up":
+        put("gate", n, i0, 7, 131)        # 6 * 16 = 96
+        put("up", n, i0, codes, sbytes)
+        put("down", n, n, 2, 127)
+        ref = 96.0 * dq
+    else:
+        put("gate", n, i0, 7, 131)
+        put("up", n, i0, 2, 127)
+        put("down", n, n, codes, sbytes)  # row m: dq(m) at column m
+        ref = 96.0 * dq
+    return W, ref
+
+
+@pytest.mark.parametrize("test", ["gate", "up", "down"])
+def test_mxfp4_decode_every_code_on_gpu(k3, test):
+    """The kernels' MXFP4 decode, matrix by matrix, for all 16 E2M1 codes
+    (both signed zeros included) under 8 scale bytes each, through the GEMV
+    (T = 1) and the grouped MFMA GEMM (T = 8): with a one-hot x every gate or
+    up output is one dequantised weight, and the down projection reads one
+    weight per output. Up and down outputs are exact products in fp32 (the
+    two-term split represents them exactly), so both paths must match bit for
+    bit; gate outputs pass through SiLU, checked to fp32 rounding on the GEMV
+    and to the split's bound (relative to each 32-row block) on the GEMM."""
+    cfg = DEQ
+    i0 = 37
+    W, ref = _one_weight_matrices(test, i0)
+    s = Custom(cfg, W)
+    layer = _layer(k3, cfg, s.dw, 8)
+    for T in (1, 8):
+        xb = np.zeros((T, cfg.d), np.uint16)
+        xb[:, i0] = 0x3F80  # bf16 1.0
+        idx = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+        gate = torch.ones((T, 1), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+        k3.k3moe_experts_forward(layer.handle, _x_dev(xb), idx, gate, y)
+        torch.cuda.synchronize()
+        yv = y.cpu().numpy().astype(np.float64)
+        for t in range(T):
+            if test != "gate":
+                bad = np.flatnonzero(yv[t] != ref)
+                assert bad.size == 0, f"T={T} {test}: rows {bad[:8]} give {yv[t][bad[:8]]}, want {ref[bad[:8]]}"
+            else:
+                blockmax = np.repeat(np.abs(ref).reshape(-1, 32).max(axis=1), 32)
+                tol = (4e-7 * np.abs(ref) + 1e-7 * blockmax) if T == 1 else (2.0 ** -7 * np.abs(ref) + 2.0 ** -14 * blockmax)
+                err = np.abs(yv[t] - ref)
+                assert np.all(err <= tol), f"T={T} gate: worst row {int(np.argmax(err / tol))}"
+    layer.close()
+
+
 def test_batch_invariance(k3):
     """A token's output does not depend on the batch it is in (chunk-union
     prefill equals the per-token path). Within the grouped-GEMM path only the
