@@ -205,6 +205,29 @@ def test_layer_forward_small(k3, cfg, T):
     layer.close()
 
 
+TOP1 = synth.LayerConfig("top1_d256_e16_k1_f256", 256, 16, 1, 256, 1, 14)
+ALLK = synth.LayerConfig("allk_d256_e8_k8_f256", 256, 8, 8, 256, 1, 15)
+
+
+@pytest.mark.parametrize("cfg", [TOP1, ALLK], ids=["k=1", "k=E"])
+def test_routing_extremes(k3, cfg):
+    """top-1: every gate is exactly 1.0; top-k = E: every expert is selected,
+    in (logit desc, index asc) order, and the gates are a full softmax (sum 1).
+    Outputs against the oracle on both paths."""
+    s = Small(cfg, 24)
+    layer = _layer(k3, cfg, s.dw, 24)
+    for T in (1, 3, 24):
+        x = synth.gen_x(cfg, T=T)
+        _, idx, gate = _run_and_check(k3, layer, cfg, x, s.src, s.wr, s.bias,
+                                      label=f"{cfg.name} T={T}")
+        if cfg.k == 1:
+            assert np.all(gate == 1.0), f"T={T}: top-1 gate is not exactly 1"
+        else:
+            assert np.all(np.sort(idx, axis=1) == np.arange(cfg.E)), f"T={T}: not every expert"
+            assert np.all(np.abs(gate.astype(np.float64).sum(axis=1) - 1.0) < 1e-6)
+    layer.close()
+
+
 def test_skewed_bias_small(k3):
     cfg = synth.LayerConfig("small_skew", 2048, 64, 8, 1024, 96, 5, skew_bias=True)
     s = Small(cfg, 96)
