@@ -90,12 +90,14 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 
 // Large T: a GEMM of the 3 weight terms [E][d] by x [T][d] on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16). Workgroup tile: 128 experts x 128 tokens; its
-// 4 waves are 2 x 2, each 64 experts x 64 tokens (4 x 4 MFMA tiles). K is
+// 8 waves are 2 x 4, each 64 experts x 32 tokens (4 x 2 MFMA tiles), and
+// each issues half as many copies as with 4 waves per workgroup (the copies
+// bound this kernel, and each wave keeps only so many in flight). K is
 // walked 32 columns at a time through a ring of 4 LDS stages, copies issued
 // 3 steps ahead. Each MFMA operand (16 rows x 32 columns) is copied straight
 // into LDS in operand order (lane l's 16 bytes = row l % 16, columns
-// 8 (l / 16) .. +7), so its read is one conflict-free ds_read_b128. The copies
-// are bounds-checked buffer loads (rows past E or T read zeros).
+// 8 (l / 16) .. +7), so its read is one conflict-free ds_read_b128. The
+// copies are bounds-checked buffer loads (rows past E or T read zeros).
 // MFMA operand lane l: row/column l % 16, 8 consecutive K at 8 (l / 16); both
 // operands use the same layout, so any consistent K order is a valid sum.
 constexpr int kRtStages = 4;
@@ -112,8 +114,10 @@ __device__ __forceinline__ void router_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// grid: (ceil(E / 128), ceil(T / 128)), block 256.
-__global__ __launch_bounds__(256, 1) void router_mfma_kernel(const uint16_t* __restrict__ x, int T,
+// grid: (ceil(E / 128), ceil(T / 128)), block 512: 8 waves, 2 x 4, each 64
+// experts x 32 tokens; copies split 4 per wave (waves 0-5: weight term
+// w / 2, row tiles 4 (w % 2) .. +3; waves 6-7: x tiles 4 (w - 6) .. +3).
+__global__ __launch_bounds__(512, 1) void router_mfma_kernel(const uint16_t* __restrict__ x, int T,
                                                              int d, const uint16_t* __restrict__ w3,
                                                              const float* __restrict__ bias, int E,
                                                              float* __restrict__ logits) {
@@ -123,53 +127,49 @@ __global__ __launch_bounds__(256, 1) void router_mfma_kernel(const uint16_t* __r
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int e0 = blockIdx.x * 128, t0 = blockIdx.y * 128;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nk = d >> 5;  // K steps
-  // copies: 32 per stage (24 weight tiles: term q, row tile i; 8 x tiles),
-  // 8 per wave: wave w < 3 takes weight term w, wave 3 takes x
+  const int wm = wave >> 2, wn = wave & 3;
+  const int nk = d >> 5;
   const size_t plane = (size_t)E * d;
-  const __amdgpu_buffer_rsrc_t rs = (wave < 3)
-      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w3 + wave * plane), 0,
+  const bool wcopy = wave < 6;
+  const int term = wave >> 1, rt0 = 4 * (wave & 1), xt0 = 4 * (wave - 6);
+  const __amdgpu_buffer_rsrc_t rs = wcopy
+      ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w3 + term * plane), 0,
                                           (int)(plane * 2), 0x00020000)
       : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, (int)((size_t)T * d * 2),
                                           0x00020000);
-  const int row0 = (wave < 3) ? e0 : t0;
-  // lane l copies row row0 + 16 i + l % 16, bytes 16 (l / 16) .. of the step's 64
+  const int row0 = wcopy ? e0 + 16 * rt0 : t0 + 16 * xt0;
   const uint32_t voff = (uint32_t)(row0 + r) * (uint32_t)d * 2u + 16u * (uint32_t)g;
-  auto issue = [&](RouterStage& S, int ks) {
-    const int kb = 64 * min(ks, nk - 1);  // byte offset of the step's columns (clamped tail)
+  auto issue = [&](RouterStage& S, int ks) __attribute__((always_inline)) {
+    const int kb = 64 * min(ks, nk - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint8_t* dst = (wave < 3) ? &S.a[wave][i][0] : &S.b[i][0];
+    for (int i = 0; i < 4; ++i) {
+      uint8_t* dst = wcopy ? &S.a[term][rt0 + i][0] : &S.b[xt0 + i][0];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16,
                                                (int)(voff + (uint32_t)i * 16u * (uint32_t)d * 2u),
                                                kb, 0, 0);
     }
   };
-  v4f acc[4][4];
+  v4f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const RouterStage& S) {
-    v8bf b[4];
+    for (int j = 0; j < 2; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const RouterStage& S) __attribute__((always_inline)) {
+    v8bf b[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v8bf*>(&S.b[4 * wn + j][16 * lane]);
+    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const v8bf*>(&S.b[2 * wn + j][16 * lane]);
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v8bf a = *reinterpret_cast<const v8bf*>(&S.a[q][4 * wm + i][16 * lane]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
   };
-  // every wave issues 8 copies per step, so at step s the copies of steps
-  // s + 1 and s + 2 (16) may still be in flight; the stage freed by step
-  // s - 1 takes step s + 3
-  auto step = [&](const RouterStage& Sc, RouterStage& Sn, int s) {
-    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(16)
+  auto step = [&](const RouterStage& Sc, RouterStage& Sn, int s) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(8)
     router_barrier();
     issue(Sn, s + 3);
     compute(Sc);
@@ -186,11 +186,11 @@ __global__ __launch_bounds__(256, 1) void router_mfma_kernel(const uint16_t* __r
     if (s + 3 >= nk) break;
     step(st3, st2, s + 3);
   }
-  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // no copy in flight at exit
-  // result element q of lane l: expert 64 wm + 16 i + 4 g + q, token 64 wn + 16 j + r
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+  // result element q of lane l: expert 64 wm + 16 i + 4 g + q, token 32 wn + 16 j + r
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + 64 * wn + 16 * j + r;
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 32 * wn + 16 * j + r;
     if (t >= T) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -223,7 +223,7 @@ hipError_t launch_router_logits(const uint16_t* x, int T, const Shape& s, const 
       hipLaunchKernelGGL(router_gemv_kernel<8>, grid, dim3(256), 0, st, x, T, s.d, wr, bias, s.E, logits);
   } else {
     dim3 grid((s.E + 127) / 128, (T + 127) / 128);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, st, x, T, s.d, wr3, bias, s.E, logits);
+    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(512), 0, st, x, T, s.d, wr3, bias, s.E, logits);
   }
   return hipGetLastError();
 }
