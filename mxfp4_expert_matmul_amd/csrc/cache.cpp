@@ -25,6 +25,7 @@
 
 #include "k3_kernels.h"
 #include "k3moe.h"
+#include "k3moe_internal.h"
 #include "lru.h"
 
 namespace {
@@ -72,6 +73,8 @@ struct k3moe_cache {
   // only what orders the calls' kernels across streams
   bool device_plan;
   void* tab_mem;                   // the tables' allocation
+  float* logits_dev;               // [max_tokens][E] router logits (device-planned)
+  const float* sel_bias;           // the router bias when it only ranks the experts, else NULL
   k3::CacheTables tb;
   k3::FillPlan fp;
   hipEvent_t plan_ev;              // recorded after the last plan kernel
@@ -100,6 +103,7 @@ void release(k3moe_cache* c) {
   if (c->pf_ev) (void)hipEventDestroy(c->pf_ev);
   if (c->plan_ev) (void)hipEventDestroy(c->plan_ev);
   (void)hipFree(c->tab_mem);
+  (void)hipFree(c->logits_dev);
   k3moe_destroy(c->route);
   k3moe_destroy(c->arena);
   (void)hipFree(c->mem);
@@ -211,27 +215,26 @@ int forward_device_planned(k3moe_cache* c, const void* x, int32_t T, float* y, i
   const int E = c->cfg.n_experts, S = c->n_slots;
   unsigned long long cap = 0;
   if (!capture_id(st, cap)) return fail(c, K3MOE_EHIP, st);
-  // 1. route over all experts (nothing read back)
-  int rc = k3moe_route(c->route, x, T, nullptr, c->idx_dev, c->gate_dev, st);
+  // 1. router logits over all experts (nothing read back)
+  int rc = k3::route_logits(c->route, x, T, c->logits_dev, st);
   if (rc != K3MOE_OK) return fail(c, rc, st);
   // 2. an earlier prefetch's copies land, and the previous plan has run,
-  // before this plan reads the tables; then plan and copy in the misses
+  // before this plan reads the tables; then the top k and the plan in one
+  // kernel (which also writes the caller's idx and gate), and the copies of
+  // the misses
   if (c->pf_pending && wait_other(st, cap, c->pf_ev, c->pf_stream, c->pf_cap) != hipSuccess)
     return fail(c, K3MOE_EHIP, st);
   c->pf_pending = false;
   if (plan_begin(c, st, cap) != hipSuccess ||
-      k3::launch_cache_plan_forward(c->idx_dev, P, E, S, c->tb, c->sidx_dev, st) != hipSuccess ||
+      k3::launch_cache_plan_forward(c->logits_dev, T, c->cfg.top_k, c->sel_bias, E, S, c->tb,
+                                    c->idx_dev, c->gate_dev, topk_idx, topk_gate, c->sidx_dev,
+                                    st) != hipSuccess ||
       plan_end(c, st, cap) != hipSuccess ||
       k3::launch_cache_fill(c->tb.fwd_copies, P, E, S, c->fp, st) != hipSuccess)
     return fail(c, K3MOE_EHIP, st);
   // 3. the expert kernels over the arena, with the selection renamed to slots
   rc = k3moe_experts_forward(c->arena, x, T, c->sidx_dev, c->gate_dev, y, st);
   if (rc != K3MOE_OK) return fail(c, rc, st);
-  if ((topk_idx && hipMemcpyAsync(topk_idx, c->idx_dev, (size_t)P * 4, hipMemcpyDeviceToDevice,
-                                  st) != hipSuccess) ||
-      (topk_gate && hipMemcpyAsync(topk_gate, c->gate_dev, (size_t)P * 4,
-                                   hipMemcpyDeviceToDevice, st) != hipSuccess))
-    return fail(c, K3MOE_EHIP, st);
   return K3MOE_OK;
 }
 
@@ -303,8 +306,9 @@ int k3moe_cache_create_ex(const k3moe_config* cfg, const k3moe_host_weights* w, 
   const size_t tab_bytes = device_plan ? E * 4 + S * 4 + S * 8 + S * 8 + S * 4 +
                                              k3::kCacheCounters * 8 + 2 * (1 + 2 * S) * 4 + 64
                                        : 0;
+  const size_t logit_bytes = device_plan ? (size_t)cfg->max_tokens * E * 4 : 0;
   // refuse before allocating: the arena, two workspaces, the selection buffers
-  if (total + 2 * (size_t)ws + 3 * P * 4 + tab_bytes > free_b) {
+  if (total + 2 * (size_t)ws + 3 * P * 4 + tab_bytes + logit_bytes > free_b) {
     delete c;
     return K3MOE_ENOMEM;
   }
@@ -317,7 +321,8 @@ int k3moe_cache_create_ex(const k3moe_config* cfg, const k3moe_host_weights* w, 
   ok = ok && hipHostMalloc(reinterpret_cast<void**>(&c->idx_host), P * 4, 0) == hipSuccess;
   ok = ok && hipHostMalloc(reinterpret_cast<void**>(&c->sidx_host), P * 4, 0) == hipSuccess;
   if (ok && device_plan) {
-    ok = hipMalloc(&c->tab_mem, tab_bytes) == hipSuccess;
+    ok = hipMalloc(&c->tab_mem, tab_bytes) == hipSuccess &&
+         hipMalloc(reinterpret_cast<void**>(&c->logits_dev), logit_bytes) == hipSuccess;
     if (ok) {
       // 8-byte fields first, then the 4-byte ones
       int64_t* p8 = static_cast<int64_t*>(c->tab_mem);
@@ -346,6 +351,7 @@ int k3moe_cache_create_ex(const k3moe_config* cfg, const k3moe_host_weights* w, 
       c->fp.bytes[t] = c->bytes[t];
     }
     c->fp.total = c->expert_total;
+    c->sel_bias = (cfg->flags & K3MOE_FLAG_BIAS_SELECT_ONLY) ? w->router_b : nullptr;
     if (reset_tables(c, true) != hipSuccess ||
         k3::prepare_cache_plan((int)std::min(P, S), (int)E, (int)S) != hipSuccess ||
         hipEventCreateWithFlags(&c->plan_ev, hipEventDisableTiming) != hipSuccess) {

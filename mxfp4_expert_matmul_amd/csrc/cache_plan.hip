@@ -9,6 +9,7 @@
 #include <climits>
 
 #include "k3_kernels.h"
+#include "topk_device.h"
 
 namespace k3 {
 
@@ -92,17 +93,23 @@ __device__ __forceinline__ bool place(const CacheTables& tb, int e, int v, int S
 
 }  // namespace
 
-// One workgroup plans a forward over the selection idx[0..P) (entries
-// outside [0, E) are dropped pairs), P <= S: the distinct experts in order
-// of first appearance; the resident ones are hits and their slots are marked
-// used first; each other one takes the least recently used slot the call does
-// not use (ties to the lower slot) and is listed for copying; every slot the
-// call uses becomes a plain resident one, last used by this forward. Writes
-// the selection renamed to slots (dropped pairs -1) and the copy list.
+// One workgroup routes and plans a forward. First each wave selects the top
+// k of its tokens' logits [T][E] (the selection and gates of the top-k
+// kernel, by the same code: topk_device.h) and writes idx and gate [T][k]
+// (and the caller's copies when given). Then it plans over the selection
+// (P = T k <= S): the distinct experts in order of first appearance; the
+// resident ones are hits and their slots are marked used first; each other
+// one takes the least recently used slot the call does not use (ties to the
+// lower slot) and is listed for copying; every slot the call uses becomes a
+// plain resident one, last used by this forward. Writes the selection
+// renamed to slots (dropped pairs -1) and the copy list.
+template <int V>  // logits per lane: E <= 64 V
 __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
-    const int32_t* __restrict__ idx, int P, int E, int S, CacheTables tb,
-    int32_t* __restrict__ sidx) {
+    const float* __restrict__ logits, int T, int k, const float* __restrict__ sel_bias, int E,
+    int S, CacheTables tb, int32_t* __restrict__ idx, float* __restrict__ gate,
+    int32_t* __restrict__ user_idx, float* __restrict__ user_gate, int32_t* __restrict__ sidx) {
   extern __shared__ __attribute__((aligned(16))) uint8_t plan_lds[];
+  const int P = T * k;
   uint64_t* key = reinterpret_cast<uint64_t*>(plan_lds);  // [S8] victim keys
   int64_t* lu = reinterpret_cast<int64_t*>(key + round8(S));  // [S] last use
   int32_t* first = reinterpret_cast<int32_t*>(lu + S);  // [E] first position in the selection
@@ -110,10 +117,27 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
   int32_t* uniq = sel + P;                               // [P] distinct experts
   int32_t* missv = uniq + P;                             // [P] those not resident
   int32_t* vict = missv + P;                             // [P] their slots
+  __shared__ __attribute__((aligned(16))) uint64_t tk_cand[kPlanThreads / 64][kTopkCand];
+  __shared__ uint64_t tk_sel[kPlanThreads / 64][64];
   __shared__ int wsum[4];
   __shared__ int64_t s_call;
   __shared__ int s_hits, s_pfh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the top k of each token (waves work alone: wave-private LDS)
+  for (int t = wave; t < T; t += kPlanThreads / 64) {
+    const float* row = logits + (size_t)t * E;
+    const uint64_t mine = topk_token<V>(row, E, k, tk_cand[wave], tk_sel[wave], sel_bias);
+    const float g = sel_bias ? topk_gate_unbiased(mine, k, row) : topk_gate_of(mine, k);
+    if (lane < k) {
+      const int e = topk_key_index(mine);
+      const size_t o = (size_t)t * k + lane;
+      idx[o] = e;
+      gate[o] = g;
+      sel[o] = e;
+      if (user_idx) user_idx[o] = e;
+      if (user_gate) user_gate[o] = g;
+    }
+  }
   if (tid == 0) {
     s_call = tb.ctr[kCtrStamp] + 1;
     tb.ctr[kCtrStamp] = s_call;
@@ -122,7 +146,6 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_forward_kernel(
   }
   for (int s = tid; s < S; s += kPlanThreads) lu[s] = tb.last_use[s];
   for (int e = tid; e < E; e += kPlanThreads) first[e] = INT_MAX;
-  for (int p = tid; p < P; p += kPlanThreads) sel[p] = idx[p];
   __syncthreads();
   const int64_t call = s_call;
   for (int p = tid; p < P; p += kPlanThreads) {
@@ -331,9 +354,15 @@ size_t cache_plan_prefetch_lds(int E, int S) {
   return (size_t)((S + 7) & ~7) * 8 + (size_t)S * 13 + (size_t)E * 12;
 }
 
+// the plan kernel instantiation for E experts: logits per lane V, E <= 64 V
+static const void* plan_forward_fn(int E) {
+  if (E <= 256) return reinterpret_cast<const void*>(cache_plan_forward_kernel<4>);
+  if (E <= 1024) return reinterpret_cast<const void*>(cache_plan_forward_kernel<16>);
+  return reinterpret_cast<const void*>(cache_plan_forward_kernel<64>);
+}
+
 hipError_t prepare_cache_plan(int P, int E, int S) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(cache_plan_forward_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute(plan_forward_fn(E), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)cache_plan_forward_lds(P, E, S));
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(cache_plan_prefetch_kernel),
@@ -341,10 +370,20 @@ hipError_t prepare_cache_plan(int P, int E, int S) {
                              (int)cache_plan_prefetch_lds(E, S));
 }
 
-hipError_t launch_cache_plan_forward(const int32_t* idx, int P, int E, int S, const CacheTables& tb,
+hipError_t launch_cache_plan_forward(const float* logits, int T, int k, const float* sel_bias,
+                                     int E, int S, const CacheTables& tb, int32_t* idx,
+                                     float* gate, int32_t* user_idx, float* user_gate,
                                      int32_t* sidx, hipStream_t st) {
-  hipLaunchKernelGGL(cache_plan_forward_kernel, dim3(1), dim3(kPlanThreads),
-                     cache_plan_forward_lds(P, E, S), st, idx, P, E, S, tb, sidx);
+  const size_t lds = cache_plan_forward_lds(T * k, E, S);
+  if (E <= 256)
+    hipLaunchKernelGGL(cache_plan_forward_kernel<4>, dim3(1), dim3(kPlanThreads), lds, st, logits,
+                       T, k, sel_bias, E, S, tb, idx, gate, user_idx, user_gate, sidx);
+  else if (E <= 1024)
+    hipLaunchKernelGGL(cache_plan_forward_kernel<16>, dim3(1), dim3(kPlanThreads), lds, st, logits,
+                       T, k, sel_bias, E, S, tb, idx, gate, user_idx, user_gate, sidx);
+  else
+    hipLaunchKernelGGL(cache_plan_forward_kernel<64>, dim3(1), dim3(kPlanThreads), lds, st, logits,
+                       T, k, sel_bias, E, S, tb, idx, gate, user_idx, user_gate, sidx);
   return hipGetLastError();
 }
 

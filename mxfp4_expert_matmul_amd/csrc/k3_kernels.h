@@ -117,7 +117,12 @@ size_t cache_plan_forward_lds(int P, int E, int S);
 size_t cache_plan_prefetch_lds(int E, int S);
 // once per cache: raise the dynamic LDS limits of the two plan kernels
 hipError_t prepare_cache_plan(int P, int E, int S);
-hipError_t launch_cache_plan_forward(const int32_t* idx, int P, int E, int S, const CacheTables& tb,
+// routes (top k of logits [T][E], selection-only bias sel_bias or NULL) and
+// plans a forward: writes idx and gate [T][k] (and user_idx / user_gate when
+// not NULL), the renamed selection sidx and the copy list; T k <= S
+hipError_t launch_cache_plan_forward(const float* logits, int T, int k, const float* sel_bias,
+                                     int E, int S, const CacheTables& tb, int32_t* idx,
+                                     float* gate, int32_t* user_idx, float* user_gate,
                                      int32_t* sidx, hipStream_t st);
 hipError_t launch_cache_plan_prefetch(const int32_t* experts, int n, int E, int S,
                                       const CacheTables& tb, hipStream_t st);

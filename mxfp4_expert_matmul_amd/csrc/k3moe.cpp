@@ -13,6 +13,7 @@
 
 #include "k3_kernels.h"
 #include "k3moe.h"
+#include "k3moe_internal.h"
 
 using k3::Shape;
 
@@ -305,6 +306,17 @@ size_t noalloc_scratch_bytes(const k3moe_config* c, int T, bool own_routing) {
 }
 
 }  // namespace
+
+int k3::route_logits(k3moe* h, const void* x, int32_t T, float* logits, hipStream_t st) {
+  int rc = check_tokens(h, T);
+  if (rc != K3MOE_OK) return rc;
+  if (T == 0) return K3MOE_OK;
+  if (!x || !logits || !aligned(x, 16) || !aligned(logits, 4)) return K3MOE_EINVAL;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return K3MOE_EHIP;
+  return run_router(h, static_cast<const uint16_t*>(x), T, logits, nullptr, nullptr, st,
+                    /*with_topk=*/false);
+}
 
 extern "C" {
 

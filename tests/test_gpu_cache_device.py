@@ -92,6 +92,38 @@ def test_device_planned_equals_resident_and_host_counts(k3, T):
     _close(dev, model, full)
 
 
+@pytest.mark.parametrize("flags", [0, 1], ids=["bias_added", "bias_select_only"])
+def test_device_planned_skewed_bias(k3, flags):
+    """The device-planned forward selects each token's experts inside its plan
+    kernel: with the skewed router bias, added to the logits or used for the
+    selection only (K3MOE_FLAG_BIAS_SELECT_ONLY), its idx, gates and outputs
+    equal the resident layer's bit for bit, and its counts the host-planned
+    cache's (GEMV and grouped paths)."""
+    from synth.device import host_weights_to_device
+    cfg = synth.LayerConfig("small_skew", 2048, 64, 8, 1024, 96, 5, skew_bias=True)
+    assert flags in (0, k3.K3MOE_FLAG_BIAS_SELECT_ONLY)
+    W = synth.gen_weights(cfg)
+    dw = k3.pack_layer_weights(host_weights_to_device(W, synth.gen_router_w(cfg), synth.gen_bias(cfg)),
+                               cfg.E, cfg.d, cfg.f)
+    host = _host_weights(dw)
+    c = k3.Config(cfg.d, cfg.E, cfg.k, cfg.f, 6, flags)
+    full = k3.Layer(c, dw, 0)
+    dev = k3.CachedLayer(c, host, 48, 0, device_plan=True)
+    model = k3.CachedLayer(c, host, 48, 0)
+    pool = synth.gen_x(cfg, T=40, stream=17)
+    calls = [pool[0:1], pool[1:4], pool[4:10], pool[10:11], pool[11:17], pool[17:20]]
+    for i, xb in enumerate(calls):
+        x = _xd(xb)
+        r = full.forward(x)
+        o = dev.forward(x)
+        model.forward(x)
+        torch.cuda.synchronize()
+        assert _same(r, o), f"call {i} (T={xb.shape[0]}) differs"
+    st, ref = dev.stats(), model.stats()
+    assert st == ref, (st, ref)
+    _close(dev, model, full)
+
+
 def test_device_planned_prefetch_overlapped(k3):
     """Call n + 1's experts, a device array, are prefetched on a copy stream
     right after call n is enqueued (call n's kernels may still run); no
