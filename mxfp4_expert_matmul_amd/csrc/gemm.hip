@@ -414,6 +414,15 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_rs, (lds_ptr)&L.s[sterm][srow0][0], 4, (int)sc_off,
                                              4 * kt, 0, 0);
   };
+  // the same copies one row group at a time (i = kActGroups: the scales)
+  auto act_issue_one = [&](ActLds& L, int kt, int i) {
+    if (i < kActGroups)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_ptr)&L.a[term][rbase + 8 * i][0], 16,
+                                               (int)asrc[i], kt * 128, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_rs, (lds_ptr)&L.s[sterm][srow0][0], 4,
+                                               (int)sc_off, 4 * kt, 0, 0);
+  };
   // one step's loads: the copy of tile ka (clamped to the last tile so the
   // tail issues the same loads; that stage is never read), then the weights
   // of tile kw (nothing past the last tile)
@@ -453,12 +462,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   };
   // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
   // next column tile's B operands are read while this one's MFMAs run.
-  auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc) {
+  auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc,
+                     auto&& piece) {
     constexpr int P = decltype(pc)::value;
     BFrag b[2];
     b_load(L, 0, b[0]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
+      piece(ct);  // the next stages' loads, a few per column tile, in issue order
       if (ct < nct) {
         if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
         const BFrag& cb = b[ct & 1];
@@ -483,19 +494,43 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // groups of 4 tiles in sa, odd groups in sb. Step P (= c % 8): wait for
   // tile c's copies (its weights, issued earlier, have landed too), barrier,
   // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
-  // group's scale dwords when c + 3 starts one), compute tile c.
+  // group's scale dwords when c + 3 starts one), compute tile c; the loads
+  // are interleaved with tile c's column tiles.
   auto step = [&](auto pc, const ActLds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
                   ActLds& Ln, WStage& Wn, int c) {
     constexpr int P = decltype(pc)::value;
     wait_vmcnt<loads_after_act<P>()>();
     stage_barrier();
-    stage_issue(Ln, c + 1, Wn, c + kWStages - 1);
-    if constexpr (((P + kWStages - 1) & 3) == 0) {
-      s_issue(after_copies(min((c + kWStages - 1) >> 2, KG - 1)),
-              (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
-      issue_fence();
-    }
-    compute(Lc, Wc, sc, std::integral_constant<int, P & 3>());
+    const int ka = min(c + 1, KT - 1);
+    // The step's loads go out between its MFMAs, in the order the load
+    // counter arithmetic assumes: the copies of tile c + 1 (clamped as in
+    // stage_issue) three, two and two ahead of column tiles 0, 1 and 2, then
+    // the weights of tile c + kWStages - 1 (and that group's scale dwords)
+    // ahead of column tile 4. Spread this way the CU's load path takes a few
+    // requests at a time while the matrix cores stay busy; a burst of all 11
+    // or 15 at the top of the step left both idle in turn (measured: the
+    // gate/up and down GEMMs 2-3% faster; weights one column tile earlier or
+    // later, or the copies over two or four column tiles, were slower).
+    static_assert(kActOps == 7 && NCT >= 5, "the 3/2/2 split below covers 7 copies");
+    compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [&](int ct) {
+      if (ct < 3) {
+        issue_fence();
+        const int i0 = ct == 0 ? 0 : (ct == 1 ? 3 : 5);
+        const int n = ct == 0 ? 3 : 2;
+#pragma unroll
+        for (int i = 0; i < n; ++i) act_issue_one(Ln, ka, i0 + i);
+        issue_fence();
+      } else if (ct == 4) {
+        issue_fence();
+        w_issue(after_copies(c + kWStages - 1), Wn);
+        issue_fence();
+        if constexpr (((P + kWStages - 1) & 3) == 0) {
+          s_issue(after_copies(min((c + kWStages - 1) >> 2, KG - 1)),
+                  (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
+          issue_fence();
+        }
+      }
+    });
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
