@@ -206,6 +206,9 @@ constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 term
 constexpr int kScRows = 128;  // scale rows per term in LDS: two waves copy 64 each (rows past
                               // the tile's tokens read nothing)
 constexpr int kActOps = kActGroups + 1;
+// column tiles (of 16 tokens) from which a workgroup interleaves its loads
+// with its MFMAs (the K loop below)
+constexpr int kSpreadMinCols = 4;
 constexpr int kWOps = 4;  // NM * NRT for both modes
 // Counted at the top of the step that computes tile c (P = c % 8): tile c's
 // copies went out one step earlier, followed only by the weights of tile
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   struct WStage {
     v4i q[NM][NRT];
   };
-  auto w_issue = [&](int kt, WStage& ws) {
+  auto w_issue = [&](int kt, WStage& ws) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // scale dwords of groups of 4 K tiles: even groups in sa, odd groups in sb
   // (two named sets, each live across the loop, so no copy is needed)
   int sa[NM][NRT], sb[NM][NRT];
-  auto s_issue = [&](int kg, int (&dst)[NM][NRT]) {
+  auto s_issue = [&](int kg, int (&dst)[NM][NRT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   }
   const int srow = srow0 + lane;
   const uint32_t sc_off = srow < ti.cnt ? (uint32_t)tok_lds[srow] * (uint32_t)nb : kNoRead;
-  auto act_issue = [&](ActLds& L, int kt) {
+  auto act_issue = [&](ActLds& L, int kt) __attribute__((always_inline)) {
     const int kb = kt * 128;
 #pragma unroll
     for (int i = 0; i < kActGroups; ++i)
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
                                              4 * kt, 0, 0);
   };
   // the same copies one row group at a time (i = kActGroups: the scales)
-  auto act_issue_one = [&](ActLds& L, int kt, int i) {
+  auto act_issue_one = [&](ActLds& L, int kt, int i) __attribute__((always_inline)) {
     if (i < kActGroups)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(act_rs, (lds_ptr)&L.a[term][rbase + 8 * i][0], 16,
                                                (int)asrc[i], kt * 128, 0, 0);
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // one step's loads: the copy of tile ka (clamped to the last tile so the
   // tail issues the same loads; that stage is never read), then the weights
   // of tile kw (nothing past the last tile)
-  auto stage_issue = [&](ActLds& L, int ka, WStage& ws, int kw) {
+  auto stage_issue = [&](ActLds& L, int ka, WStage& ws, int kw) __attribute__((always_inline)) {
     ka = min(ka, KT - 1);
     issue_fence();
     act_issue(L, ka);
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     issue_fence();
   };
 
+  auto k_loop = [&](auto sp) __attribute__((always_inline)) {
   v4f acc[NM][NRT][NCT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     v8i hi, lo;
     int shi, slo;
   };
-  auto b_load = [&](const ActLds& L, int ct, BFrag& b) {
+  auto b_load = [&](const ActLds& L, int ct, BFrag& b) __attribute__((always_inline)) {
     const int tr = m0 + 16 * ct + r;
     const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
     b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
@@ -463,13 +467,13 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
   // next column tile's B operands are read while this one's MFMAs run.
   auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc,
-                     auto&& piece) {
+                     auto&& piece) __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     BFrag b[2];
     b_load(L, 0, b[0]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      piece(ct);  // the next stages' loads, a few per column tile, in issue order
+      piece(ct);  // loads issued ahead of this column tile (if any)
       if (ct < nct) {
         if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
         const BFrag& cb = b[ct & 1];
@@ -494,43 +498,63 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   // groups of 4 tiles in sa, odd groups in sb. Step P (= c % 8): wait for
   // tile c's copies (its weights, issued earlier, have landed too), barrier,
   // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
-  // group's scale dwords when c + 3 starts one), compute tile c; the loads
-  // are interleaved with tile c's column tiles.
-  auto step = [&](auto pc, const ActLds& Lc, const WStage& Wc, const int (&sc)[NM][NRT],
-                  ActLds& Ln, WStage& Wn, int c) {
+  // group's scale dwords when c + 3 starts one), compute tile c.
+  //
+  // Where the step's loads go (SPREAD, fixed per workgroup, so each loop is
+  // free of branches on it):
+  //  - SPREAD (tiles of at least kSpreadMinCols column tiles): between the
+  //    MFMAs, in the order the load counter arithmetic assumes: the copies of
+  //    tile c + 1 (clamped as in stage_issue) three, two and two ahead of
+  //    column tiles 0, 1 and 2, then the weights of tile c + kWStages - 1 (and
+  //    that group's scale dwords) ahead of column tile 4, or after the last
+  //    MFMA of a tile of 4 column tiles. The CU's load path then takes a few
+  //    requests at a time while the matrix cores stay busy, instead of a burst
+  //    of 11 or 15 at the top of the step;
+  //  - otherwise all at the top of the step: a tile of few tokens is paced
+  //    by its weight stream, and the few MFMAs a later issue would wait for
+  //    only delay it.
+  // Measured (T = 4096 with skewed routing, and uniform routing at T = 5 to
+  // 4096): the layer 2.3% faster at T = 4096 than with every tile issuing at
+  // the top, and no slower at any smaller T; interleaving tiles of 1-3 column
+  // tiles as well cost 1-3% at T = 5-1024; interleaving only full tiles gained
+  // nothing. A branch on the tile size at each issue point (not one per
+  // workgroup) cost more than either order gained.
+  static_assert(kActOps == 7 && NCT >= 5, "the 3/2/2 split below covers 7 copies");
+  auto step = [&](auto pc, auto spread, const ActLds& Lc, const WStage& Wc,
+                  const int (&sc)[NM][NRT], ActLds& Ln, WStage& Wn, int c)
+      __attribute__((always_inline)) {
     constexpr int P = decltype(pc)::value;
     wait_vmcnt<loads_after_act<P>()>();
     stage_barrier();
-    const int ka = min(c + 1, KT - 1);
-    // The step's loads go out between its MFMAs, in the order the load
-    // counter arithmetic assumes: the copies of tile c + 1 (clamped as in
-    // stage_issue) three, two and two ahead of column tiles 0, 1 and 2, then
-    // the weights of tile c + kWStages - 1 (and that group's scale dwords)
-    // ahead of column tile 4. Spread this way the CU's load path takes a few
-    // requests at a time while the matrix cores stay busy; a burst of all 11
-    // or 15 at the top of the step left both idle in turn (measured: the
-    // gate/up and down GEMMs 2-3% faster; weights one column tile earlier or
-    // later, or the copies over two or four column tiles, were slower).
-    static_assert(kActOps == 7 && NCT >= 5, "the 3/2/2 split below covers 7 copies");
-    compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [&](int ct) {
-      if (ct < 3) {
+    const int kw = c + kWStages - 1;
+    auto s_issue_group = [&]() __attribute__((always_inline)) {
+      if constexpr (((P + kWStages - 1) & 3) == 0) {
+        s_issue(after_copies(min(kw >> 2, KG - 1)), (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
         issue_fence();
-        const int i0 = ct == 0 ? 0 : (ct == 1 ? 3 : 5);
-        const int n = ct == 0 ? 3 : 2;
-#pragma unroll
-        for (int i = 0; i < n; ++i) act_issue_one(Ln, ka, i0 + i);
-        issue_fence();
-      } else if (ct == 4) {
-        issue_fence();
-        w_issue(after_copies(c + kWStages - 1), Wn);
-        issue_fence();
-        if constexpr (((P + kWStages - 1) & 3) == 0) {
-          s_issue(after_copies(min((c + kWStages - 1) >> 2, KG - 1)),
-                  (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
-          issue_fence();
-        }
       }
-    });
+    };
+    if constexpr (decltype(spread)::value) {
+      const int ka = min(c + 1, KT - 1);
+      compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [&](int ct) {
+        if (ct < 3) {
+          issue_fence();
+          const int i0 = ct == 0 ? 0 : (ct == 1 ? 3 : 5);
+          const int n = ct == 0 ? 3 : 2;
+#pragma unroll
+          for (int i = 0; i < n; ++i) act_issue_one(Ln, ka, i0 + i);
+          issue_fence();
+        } else if (ct == 4) {
+          issue_fence();
+          w_issue(after_copies(kw), Wn);
+          issue_fence();
+          s_issue_group();
+        }
+      });
+    } else {
+      stage_issue(Ln, c + 1, Wn, kw);
+      s_issue_group();
+      compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [](int) {});
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -541,35 +565,35 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   using I6 = std::integral_constant<int, 6>;
   using I7 = std::integral_constant<int, 7>;
   static_assert(kWStages == 4 && kStages == 2, "the unrolled ring below assumes these depths");
-  WStage wa, wb, wc, wd;
-  stage_issue(lds0, 0, wa, 0);
-  s_issue(0, sa);
-  issue_fence();
-  w_issue(1, wb);
-  issue_fence();
-  w_issue(2, wc);
-  issue_fence();
-  for (int c = 0; c < KT; c += 8) {
-    step(I0(), lds0, wa, sa, lds1, wd, c);
-    if (c + 1 >= KT) break;
-    step(I1(), lds1, wb, sa, lds0, wa, c + 1);
-    if (c + 2 >= KT) break;
-    step(I2(), lds0, wc, sa, lds1, wb, c + 2);
-    if (c + 3 >= KT) break;
-    step(I3(), lds1, wd, sa, lds0, wc, c + 3);
-    if (c + 4 >= KT) break;
-    step(I4(), lds0, wa, sb, lds1, wd, c + 4);
-    if (c + 5 >= KT) break;
-    step(I5(), lds1, wb, sb, lds0, wa, c + 5);
-    if (c + 6 >= KT) break;
-    step(I6(), lds0, wc, sb, lds1, wb, c + 6);
-    if (c + 7 >= KT) break;
-    step(I7(), lds1, wd, sb, lds0, wc, c + 7);
-  }
-  // no copy may still be writing this workgroup's LDS when it exits. (A
-  // wave past the last row computed on the first rows' weights: discarded.)
-  wait_vmcnt<0>();
-  if (!wave_on) return;
+    WStage wa, wb, wc, wd;
+    stage_issue(lds0, 0, wa, 0);
+    s_issue(0, sa);
+    issue_fence();
+    w_issue(1, wb);
+    issue_fence();
+    w_issue(2, wc);
+    issue_fence();
+    for (int c = 0; c < KT; c += 8) {
+      step(I0(), sp, lds0, wa, sa, lds1, wd, c);
+      if (c + 1 >= KT) break;
+      step(I1(), sp, lds1, wb, sa, lds0, wa, c + 1);
+      if (c + 2 >= KT) break;
+      step(I2(), sp, lds0, wc, sa, lds1, wb, c + 2);
+      if (c + 3 >= KT) break;
+      step(I3(), sp, lds1, wd, sa, lds0, wc, c + 3);
+      if (c + 4 >= KT) break;
+      step(I4(), sp, lds0, wa, sb, lds1, wd, c + 4);
+      if (c + 5 >= KT) break;
+      step(I5(), sp, lds1, wb, sb, lds0, wa, c + 5);
+      if (c + 6 >= KT) break;
+      step(I6(), sp, lds0, wc, sb, lds1, wb, c + 6);
+      if (c + 7 >= KT) break;
+      step(I7(), sp, lds1, wd, sb, lds0, wc, c + 7);
+    }
+    // no copy may still be writing this workgroup's LDS when it exits. (A
+    // wave past the last row computed on the first rows' weights: discarded.)
+    wait_vmcnt<0>();
+    if (!wave_on) return;
 
   if constexpr (MODE == kGateUp) {
     // h = SiLU(g) * u, split into two E4M3 terms per 32 features (the wave's
@@ -672,6 +696,13 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
       }
     }
   }
+  };  // k_loop: each schedule has its own accumulators, drain and epilogue
+  // (the choice through a scalar register: the compiler does not know nct is
+  // uniform, and a masked branch here would run both loops' registers at once)
+  if (__builtin_amdgcn_readfirstlane(nct) >= kSpreadMinCols)
+    k_loop(std::true_type());
+  else
+    k_loop(std::false_type());
 }
 
 // y[t] = sum_j gate[t,j] * slot[t*k + j], j in order; pairs whose expert is
