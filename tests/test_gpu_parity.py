@@ -715,6 +715,57 @@ def test_experts_forward_injected_routing(k3):
     layer.close()
 
 
+def _routing_with_counts(counts, T, k, E, seed):
+    """idx [T][k] in which expert e is chosen by exactly counts[e] distinct
+    tokens; every other slot holds the dropped index E + 1."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((T, k), E + 1, dtype=np.int32)
+    used = np.zeros(T, dtype=np.int64)
+    for e in rng.permutation(len(counts)):
+        c = int(counts[e])
+        if c == 0:
+            continue
+        # the tokens with the most free slots (random among equals) keep it feasible
+        order = np.lexsort((rng.random(T), used))
+        toks = order[:c]
+        assert used[toks].max() < k, "counts exceed the slots"
+        idx[toks, used[toks]] = e
+        used[toks] += 1
+    for t in range(T):  # the pairs' slot order within a token, shuffled
+        idx[t] = idx[t][rng.permutation(k)]
+    return idx
+
+
+def test_tile_sizes_across_column_tile_counts(k3):
+    """The grouped GEMMs at every tile size class: experts with exactly 1,
+    15-17, 31-33, ..., 95-97 and 191-193 tokens give tiles of 1 to 6 16-token
+    column tiles, ragged and full (tiles of 96), and a third ragged tile.
+    Tiles of 4 or more column tiles and smaller ones run different K loop
+    schedules; every token is compared with the oracle."""
+    cfg = synth.CONFIGS[1]
+    T = 300
+    counts = np.zeros(cfg.E, dtype=np.int64)
+    sizes = [1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 79, 80, 81, 95, 96, 97,
+             143, 144, 145, 191, 192, 193]
+    counts[:len(sizes)] = sizes
+    idx = _routing_with_counts(counts, T, cfg.k, cfg.E, seed=31)
+    got = np.bincount(idx[idx < cfg.E], minlength=cfg.E)
+    assert np.array_equal(got, counts)
+    s = Small(cfg, T)
+    layer = _layer(k3, cfg, s.dw, T)
+    x = synth.gen_x(cfg, T=T)
+    gate = np.random.default_rng(32).random((T, cfg.k)).astype(np.float32)
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    k3.k3moe_experts_forward(layer.handle, _x_dev(x), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(gate).cuda(), y)
+    torch.cuda.synchronize()
+    yref = oracle.experts_forward(x, idx, gate.astype(np.float64), s.src, n_experts=cfg.E)
+    ratio = check_output(y.cpu().numpy(), yref, "tile sizes")
+    _say(f"[tile sizes] {len(sizes)} experts, {int(counts.sum())} pairs, "
+         f"max|err|/rms = {ratio:.3e}")
+    layer.close()
+
+
 def test_abi_rejects_bad_calls(k3):
     cfg = synth.CONFIGS[0]
     s = Small(cfg, 4)
