@@ -272,6 +272,30 @@ def test_wide_scale_exponents(k3, T):
     layer.close()
 
 
+@pytest.mark.parametrize("cfg", [EDGE, synth.CONFIGS[1]], ids=lambda c: c.name)
+@pytest.mark.parametrize("spread", [4, 16, 32, 51])
+def test_scale_spread_sweep(k3, cfg, spread):
+    """Grouped path (T = 40) with the weights' E8M0 scale bytes uniform over
+    `spread` binades about 2^-2 (4: the generator's own spread; 51: the wide
+    case above). The two-term activation split is exact to about 2^-8 of a
+    block's largest value, so the output error grows as fewer blocks dominate
+    each sum: the wider the spread and the fewer blocks per row (8 at d = 256,
+    64 at d = 2048), the larger. Logged per case; each within the bar."""
+    W = synth.gen_weights(cfg)
+    rng = np.random.default_rng(37)
+    lo = 125 - spread // 2
+    for name in ("gate_s", "up_s", "down_s"):
+        W[name] = rng.integers(lo, lo + spread, W[name].shape).astype(np.uint8)
+    s = Custom(cfg, W)
+    T = 40
+    layer = _layer(k3, cfg, s.dw, T)
+    x = synth.gen_x(cfg, T=T)
+    y, _, _ = _run_and_check(k3, layer, cfg, x, s.src, s.wr, None,
+                             label=f"scale spread {spread} {cfg.name}")
+    assert np.all(np.isfinite(y))
+    layer.close()
+
+
 @pytest.mark.parametrize("T", [3, 64])
 def test_activation_outlier_channels(k3, T):
     """Four hidden channels 32x larger than the rest (as real activations
