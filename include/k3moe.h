@@ -384,6 +384,14 @@ int k3moe_cache_device_counters(const k3moe_cache* c, int64_t* refused_prefetche
 #define K3MOE_NUM_STAGES          7
 int k3moe_profile_begin(k3moe* h, int32_t max_calls);
 int k3moe_profile_end(k3moe* h, float* total_ms, int32_t* launches);
+/* The same for the stages in stage_mask only (bit i: stage i; the others
+ * record no events and report 0 launches). Each event pair sits between two
+ * kernels on the stream and adds a few microseconds to the call, so timing
+ * one kernel inside a timed loop disturbs that loop less than timing all
+ * seven stages. k3moe_profile_begin(h, n) is stage_mask = all stages.
+ * K3MOE_EINVAL for a NULL handle, max_calls outside [1, 2^20], or a mask
+ * that is 0 or has bits at K3MOE_NUM_STAGES or above. */
+int k3moe_profile_begin_stages(k3moe* h, int32_t max_calls, uint32_t stage_mask);
 
 #ifdef __cplusplus
 }

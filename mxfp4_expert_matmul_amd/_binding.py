@@ -97,6 +97,8 @@ def load_library():
     lib.k3moe_profile_begin.restype = ctypes.c_int
     lib.k3moe_profile_end.argtypes = [vp, vp, vp]
     lib.k3moe_profile_end.restype = ctypes.c_int
+    lib.k3moe_profile_begin_stages.argtypes = [vp, i32, ctypes.c_uint32]
+    lib.k3moe_profile_begin_stages.restype = ctypes.c_int
     lib.k3moe_cache_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), i32,
                                        ctypes.c_int, ctypes.POINTER(vp)]
     lib.k3moe_cache_create.restype = ctypes.c_int

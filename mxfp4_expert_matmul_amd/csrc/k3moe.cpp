@@ -134,6 +134,7 @@ struct k3moe {
   // stage timing (k3moe_profile_begin / k3moe_profile_end)
   bool prof_on;
   int prof_cap;
+  uint32_t prof_mask;  // stages timed (bit i: stage i)
   int prof_n[K3MOE_NUM_STAGES];
   std::vector<hipEvent_t> prof_ev[K3MOE_NUM_STAGES];  // 2 per recorded launch
   // a second stream (default priority) on which the whole-layer call splits x
@@ -152,6 +153,7 @@ void profile_release(k3moe* h) {
   }
   h->prof_on = false;
   h->prof_cap = 0;
+  h->prof_mask = 0;
 }
 
 // The router bias as the logit kernels see it (added to every logit) and as
@@ -177,7 +179,7 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? K3MOE_OK : K3MOE_
 // stage timing is on.
 template <class F>
 hipError_t stage(k3moe* h, int id, hipStream_t st, F&& launch) {
-  const bool rec = h->prof_on && h->prof_n[id] < h->prof_cap;
+  const bool rec = h->prof_on && ((h->prof_mask >> id) & 1u) && h->prof_n[id] < h->prof_cap;
   if (rec) {
     hipError_t e = hipEventRecord(h->prof_ev[id][2 * h->prof_n[id]], st);
     if (e != hipSuccess) return e;
@@ -620,11 +622,17 @@ int k3moe_layer_forward_noalloc(const k3moe_config* cfg, const k3moe_weights* w,
 
 
 int k3moe_profile_begin(k3moe* h, int32_t max_calls) {
+  return k3moe_profile_begin_stages(h, max_calls, (1u << K3MOE_NUM_STAGES) - 1u);
+}
+
+int k3moe_profile_begin_stages(k3moe* h, int32_t max_calls, uint32_t stage_mask) {
   if (!h || max_calls <= 0 || max_calls > (1 << 20)) return K3MOE_EINVAL;
+  if (stage_mask == 0 || (stage_mask >> K3MOE_NUM_STAGES) != 0) return K3MOE_EINVAL;
   DeviceGuard guard(h->device);
   if (!guard.ok) return K3MOE_EHIP;
   profile_release(h);
   for (int i = 0; i < K3MOE_NUM_STAGES; ++i) {
+    if (!((stage_mask >> i) & 1u)) continue;
     try {
       h->prof_ev[i].resize(2 * (size_t)max_calls, nullptr);
     } catch (...) {
@@ -640,6 +648,7 @@ int k3moe_profile_begin(k3moe* h, int32_t max_calls) {
     }
   }
   h->prof_cap = max_calls;
+  h->prof_mask = stage_mask;
   h->prof_on = true;
   return K3MOE_OK;
 }

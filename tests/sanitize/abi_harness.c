@@ -97,6 +97,8 @@ int main(void)
     CHECK(k3moe_experts_forward(NULL, p, 1, (int32_t *)p, (float *)p, (float *)p, NULL) == K3MOE_EINVAL,
           "experts NULL");
     CHECK(k3moe_profile_begin(NULL, 4) == K3MOE_EINVAL, "profile_begin NULL");
+    CHECK(k3moe_profile_begin_stages(NULL, 4, 1u << K3MOE_STAGE_GATEUP) == K3MOE_EINVAL,
+          "profile_begin_stages NULL");
     float ms[K3MOE_NUM_STAGES];
     int32_t launches[K3MOE_NUM_STAGES];
     CHECK(k3moe_profile_end(NULL, ms, launches) == K3MOE_EINVAL, "profile_end NULL");

@@ -90,3 +90,27 @@ def test_stage_profile(k3):
     torch.cuda.synchronize()
     assert torch.equal(y0, y2)
     layer.close()
+
+
+def test_stage_profile_mask(k3):
+    """k3moe_profile_begin_stages times only the masked stages; a zero mask
+    or one with bits past the last stage is refused."""
+    lib = k3.load_library()
+    cfg = synth.CONFIGS[1]
+    layer = _layer(k3, cfg, 64)
+    h = layer.handle
+    gateup = STAGES.index("gateup")
+    assert lib.k3moe_profile_begin_stages(h, 4, 0) == k3.K3MOE_EINVAL
+    assert lib.k3moe_profile_begin_stages(h, 4, 1 << N_STAGES) == k3.K3MOE_EINVAL
+    assert lib.k3moe_profile_begin_stages(h, 0, 1 << gateup) == k3.K3MOE_EINVAL
+    for T, mask in ((40, 1 << gateup), (1, 1 << gateup), (40, (1 << gateup) | 1)):
+        assert lib.k3moe_profile_begin_stages(h, 2, mask) == k3.K3MOE_OK
+        for i in range(3):
+            layer.forward(_x(cfg, T, 50 + i))
+        rc, total, launches = _end(lib, h)
+        assert rc == k3.K3MOE_OK
+        want = [2 if (mask >> i) & 1 else 0 for i in range(N_STAGES)]
+        assert launches == want, (T, mask, launches)
+        for s, ms, n in zip(STAGES, total, launches):
+            assert (ms > 0.0) == (n > 0), (T, s, ms, n)
+    layer.close()
