@@ -201,7 +201,7 @@ struct GemmShape {
 // (kActGroups row groups + 1 scale copy), then kWOps weight tiles of tile
 // c + kWStages - 1, then, when that tile starts a group of 4, kWOps scale
 // dwords for the group. The order is pinned (compiler barriers around each
-// group).
+// group); where in the step they go depends on the tile's size (K loop).
 constexpr int kActGroups = kTileM * 2 / 8 / 4;  // 8-row groups per wave (2 terms, 4 waves)
 constexpr int kScRows = 128;  // scale rows per term in LDS: two waves copy 64 each (rows past
                               // the tile's tokens read nothing)
