@@ -57,3 +57,18 @@ def test_traffic_is_dropped_when_the_sources_change(tmp_path, monkeypatch):
     assert bench._traffic("gemv_gateup_kernel", "decode_t1") is not None
     monkeypatch.setattr(bench, "_source_hash", lambda: "1" * 16)
     assert bench._traffic("gemv_gateup_kernel", "decode_t1") is None
+
+
+def test_roofline_uses_the_timed_region_kernel_time(monkeypatch):
+    """The roofline divides the dominant kernel's algorithmic bytes by its
+    time inside the timed region, not by the separate all-stage pass."""
+    monkeypatch.setattr(bench, "_traffic", lambda kern, workload: None)
+    cfg = synth.CONFIGS[4]
+    res = {"stage_ms": {"gateup": 9.0, "down": 1.0, "router_logits": 0.1, "combine": 0.1},
+           "dominant": {"stage": "gateup", "ms": 4.0}, "experts_touched": 896}
+    r = bench.roofline_for(cfg, cfg.T, res, "prefill_t4096")
+    nbytes = bench.algorithmic_bytes(cfg, cfg.T, 896, "gateup")
+    assert r["kernel_ms"] == 4.0 and r["algorithmic_bytes"] == nbytes
+    assert r["achieved"] == round(nbytes / 4.0e-3 / 1e9, 1)
+    assert r["frac"] == round(nbytes / 4.0e-3 / 1e9 / bench.HBM_PEAK_GBS, 4)
+    assert r["kernel"] == "mx_gemm_kernel<0>"
