@@ -439,135 +439,138 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
   };
 
   auto k_loop = [&](auto sp) __attribute__((always_inline)) {
-  v4f acc[NM][NRT][NCT];
+    v4f acc[NM][NRT][NCT];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NCT; ++ct) acc[m][rt][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // B operands of one 16-token column tile: pieces g and 4 + g of the token
-  // row (K slots 16g.. and 64 + 16g.. of the MFMA), both terms, and the
-  // terms' scales of 32-column block g
-  struct BFrag {
-    v8i hi, lo;
-    int shi, slo;
-  };
-  auto b_load = [&](const ActLds& L, int ct, BFrag& b) __attribute__((always_inline)) {
-    const int tr = m0 + 16 * ct + r;
-    const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
-    b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
-                       *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
-    b.lo = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
-                       *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
-    b.shi = L.s[0][tr][g];
-    b.slo = L.s[1][tr][g];
-  };
-  // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
-  // next column tile's B operands are read while this one's MFMAs run.
-  auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc,
-                     auto&& piece) __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-    BFrag b[2];
-    b_load(L, 0, b[0]);
+    // B operands of one 16-token column tile: pieces g and 4 + g of the token
+    // row (K slots 16g.. and 64 + 16g.. of the MFMA), both terms, and the
+    // terms' scales of 32-column block g
+    struct BFrag {
+      v8i hi, lo;
+      int shi, slo;
+    };
+    auto b_load = [&](const ActLds& L, int ct, BFrag& b) __attribute__((always_inline)) {
+      const int tr = m0 + 16 * ct + r;
+      const int c0 = 16 * (g ^ (r & 7)), c1 = 16 * ((4 + g) ^ (r & 7));
+      b.hi = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[0][tr][c0]),
+                         *reinterpret_cast<const uint4*>(&L.a[0][tr][c1]));
+      b.lo = fp8_operand(*reinterpret_cast<const uint4*>(&L.a[1][tr][c0]),
+                         *reinterpret_cast<const uint4*>(&L.a[1][tr][c1]));
+      b.shi = L.s[0][tr][g];
+      b.slo = L.s[1][tr][g];
+    };
+    // one K tile of MFMAs; P = the tile's byte in the weight scale dwords. The
+    // next column tile's B operands are read while this one's MFMAs run.
+    auto compute = [&](const ActLds& L, const WStage& ws, const int (&sw)[NM][NRT], auto pc,
+                       auto&& piece) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      BFrag b[2];
+      b_load(L, 0, b[0]);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      piece(ct);  // loads issued ahead of this column tile (if any)
-      if (ct < nct) {
-        if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
-        const BFrag& cb = b[ct & 1];
+      for (int ct = 0; ct < NCT; ++ct) {
+        piece(ct);  // loads issued ahead of this column tile (if any)
+        if (ct < nct) {
+          if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
+          const BFrag& cb = b[ct & 1];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-            acc[m][rt][ct] =
-                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.hi, cb.shi, acc[m][rt][ct]);
+            for (int rt = 0; rt < NRT; ++rt)
+              acc[m][rt][ct] =
+                  mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.hi, cb.shi,
+                                  acc[m][rt][ct]);
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+          for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-            acc[m][rt][ct] =
-                mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.lo, cb.slo, acc[m][rt][ct]);
-      }
-    }
-  };
-
-  // ---- K loop: tile c's activations in LDS buffer c % 2, its weights in
-  // register set c % 4 (issued three steps ahead); scale dwords of even
-  // groups of 4 tiles in sa, odd groups in sb. Step P (= c % 8): wait for
-  // tile c's copies (its weights, issued earlier, have landed too), barrier,
-  // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
-  // group's scale dwords when c + 3 starts one), compute tile c.
-  //
-  // Where the step's loads go (SPREAD, fixed per workgroup, so each loop is
-  // free of branches on it):
-  //  - SPREAD (tiles of at least kSpreadMinCols column tiles): between the
-  //    MFMAs, in the order the load counter arithmetic assumes: the copies of
-  //    tile c + 1 (clamped as in stage_issue) three, two and two ahead of
-  //    column tiles 0, 1 and 2, then the weights of tile c + kWStages - 1 (and
-  //    that group's scale dwords) ahead of column tile 4 (gate/up; after the
-  //    last MFMA of a tile of 4 column tiles) or 3 (down). The CU's load path then takes a few
-  //    requests at a time while the matrix cores stay busy, instead of a burst
-  //    of 11 or 15 at the top of the step;
-  //  - otherwise all at the top of the step: a tile of few tokens is paced
-  //    by its weight stream, and the few MFMAs a later issue would wait for
-  //    only delay it.
-  // Measured (T = 4096 with skewed routing, and uniform routing at T = 5 to
-  // 4096): the layer 2.3% faster at T = 4096 than with every tile issuing at
-  // the top, and no slower at any smaller T; interleaving tiles of 1-3 column
-  // tiles as well cost 1-3% at T = 5-1024; interleaving only full tiles gained
-  // nothing. A branch on the tile size at each issue point (not one per
-  // workgroup) cost more than either order gained.
-  static_assert(kActOps == 7 && NCT >= 5, "the 3/2/2 split below covers 7 copies");
-  auto step = [&](auto pc, auto spread, const ActLds& Lc, const WStage& Wc,
-                  const int (&sc)[NM][NRT], ActLds& Ln, WStage& Wn, int c)
-      __attribute__((always_inline)) {
-    constexpr int P = decltype(pc)::value;
-    wait_vmcnt<loads_after_act<P>()>();
-    stage_barrier();
-    const int kw = c + kWStages - 1;
-    auto s_issue_group = [&]() __attribute__((always_inline)) {
-      if constexpr (((P + kWStages - 1) & 3) == 0) {
-        s_issue(after_copies(min(kw >> 2, KG - 1)), (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
-        issue_fence();
+            for (int rt = 0; rt < NRT; ++rt)
+              acc[m][rt][ct] =
+                  mfma_fp4_fp8<P>(fp4_operand(ws.q[m][rt]), sw[m][rt], cb.lo, cb.slo,
+                                  acc[m][rt][ct]);
+        }
       }
     };
-    if constexpr (decltype(spread)::value) {
-      // the weights' column tile: 4 for gate/up, 3 for down (measured: down
-      // 0.5-0.9% faster with 3 than with 4, gate/up slower with 3)
-      constexpr int kWeightsAt = MODE == kDown ? 3 : 4;
-      const int ka = min(c + 1, KT - 1);
-      compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [&](int ct) {
-        if (ct < 3) {
+
+    // ---- K loop: tile c's activations in LDS buffer c % 2, its weights in
+    // register set c % 4 (issued three steps ahead); scale dwords of even
+    // groups of 4 tiles in sa, odd groups in sb. Step P (= c % 8): wait for
+    // tile c's copies (its weights, issued earlier, have landed too), barrier,
+    // issue the copy of tile c + 1 and the weights of tile c + 3 (with that
+    // group's scale dwords when c + 3 starts one), compute tile c.
+    //
+    // Where the step's loads go (SPREAD, fixed per workgroup, so each loop is
+    // free of branches on it):
+    //  - SPREAD (tiles of at least kSpreadMinCols column tiles): between the
+    //    MFMAs, in the order the load counter arithmetic assumes: the copies
+    //    of tile c + 1 (clamped as in stage_issue) three, two and two ahead
+    //    of column tiles 0, 1 and 2, then the weights of tile c + kWStages - 1
+    //    (and that group's scale dwords) ahead of column tile 4 (gate/up;
+    //    after the last MFMA of a tile of 4 column tiles) or 3 (down). The
+    //    CU's load path then takes a few requests at a time while the matrix
+    //    cores stay busy, instead of a burst of 11 or 15 at the top of the
+    //    step;
+    //  - otherwise all at the top of the step: a tile of few tokens is paced
+    //    by its weight stream, and the few MFMAs a later issue would wait for
+    //    only delay it.
+    // Measured (T = 4096 with skewed routing, and uniform routing at T = 5 to
+    // 4096): the layer 2.3% faster at T = 4096 than with every tile issuing at
+    // the top, and no slower at any smaller T; interleaving tiles of 1-3 column
+    // tiles as well cost 1-3% at T = 5-1024; interleaving only full tiles gained
+    // nothing. A branch on the tile size at each issue point (not one per
+    // workgroup) cost more than either order gained.
+    static_assert(kActOps == 7 && NCT >= 5, "the 3/2/2 split below covers 7 copies");
+    auto step = [&](auto pc, auto spread, const ActLds& Lc, const WStage& Wc,
+                    const int (&sc)[NM][NRT], ActLds& Ln, WStage& Wn, int c)
+        __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      wait_vmcnt<loads_after_act<P>()>();
+      stage_barrier();
+      const int kw = c + kWStages - 1;
+      auto s_issue_group = [&]() __attribute__((always_inline)) {
+        if constexpr (((P + kWStages - 1) & 3) == 0) {
+          s_issue(after_copies(min(kw >> 2, KG - 1)), (((P + kWStages - 1) >> 2) & 1) ? sb : sa);
           issue_fence();
-          const int i0 = ct == 0 ? 0 : (ct == 1 ? 3 : 5);
-          const int n = ct == 0 ? 3 : 2;
-#pragma unroll
-          for (int i = 0; i < n; ++i) act_issue_one(Ln, ka, i0 + i);
-          issue_fence();
-        } else if (ct == kWeightsAt) {
-          issue_fence();
-          w_issue(after_copies(kw), Wn);
-          issue_fence();
-          s_issue_group();
         }
-      });
-    } else {
-      stage_issue(Ln, c + 1, Wn, kw);
-      s_issue_group();
-      compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [](int) {});
-    }
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-  using I6 = std::integral_constant<int, 6>;
-  using I7 = std::integral_constant<int, 7>;
-  static_assert(kWStages == 4 && kStages == 2, "the unrolled ring below assumes these depths");
+      };
+      if constexpr (decltype(spread)::value) {
+        // the weights' column tile: 4 for gate/up, 3 for down (measured: down
+        // 0.5-0.9% faster with 3 than with 4, gate/up slower with 3)
+        constexpr int kWeightsAt = MODE == kDown ? 3 : 4;
+        const int ka = min(c + 1, KT - 1);
+        compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [&](int ct) {
+          if (ct < 3) {
+            issue_fence();
+            const int i0 = ct == 0 ? 0 : (ct == 1 ? 3 : 5);
+            const int n = ct == 0 ? 3 : 2;
+#pragma unroll
+            for (int i = 0; i < n; ++i) act_issue_one(Ln, ka, i0 + i);
+            issue_fence();
+          } else if (ct == kWeightsAt) {
+            issue_fence();
+            w_issue(after_copies(kw), Wn);
+            issue_fence();
+            s_issue_group();
+          }
+        });
+      } else {
+        stage_issue(Ln, c + 1, Wn, kw);
+        s_issue_group();
+        compute(Lc, Wc, sc, std::integral_constant<int, P & 3>(), [](int) {});
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    static_assert(kWStages == 4 && kStages == 2, "the unrolled ring below assumes these depths");
     WStage wa, wb, wc, wd;
     stage_issue(lds0, 0, wa, 0);
     s_issue(0, sa);
@@ -598,107 +601,108 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
     wait_vmcnt<0>();
     if (!wave_on) return;
 
-  if constexpr (MODE == kGateUp) {
-    // h = SiLU(g) * u, split into two E4M3 terms per 32 features (the wave's
-    // 32 features are one MX block; lane (r, g) holds features 16 rt + 4 g + i
-    // of token column r).
-    const int nbf = f_out >> 5;
+    if constexpr (MODE == kGateUp) {
+      // h = SiLU(g) * u, split into two E4M3 terms per 32 features (the wave's
+      // 32 features are one MX block; lane (r, g) holds features 16 rt + 4 g + i
+      // of token column r).
+      const int nbf = f_out >> 5;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if (ct >= nct) continue;
-      float h[2][4];
-      float amax = 0.0f;
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (ct >= nct) continue;
+        float h[2][4];
+        float amax = 0.0f;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[rt][i] = silu_f32(acc[0][rt][ct][i]) * acc[NM - 1][rt][ct][i];
-          amax = fmaxf(amax, fabsf(h[rt][i]));
+          for (int i = 0; i < 4; ++i) {
+            h[rt][i] = silu_f32(acc[0][rt][ct][i]) * acc[NM - 1][rt][ct][i];
+            amax = fmaxf(amax, fabsf(h[rt][i]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const uint32_t b1 = e4m3_block_scale_byte(amax);
+        const float s1 = e8m0_to_f32(b1), s1inv = e8m0_to_f32(254u - b1);
+        float hi[2][4], rs[2][4];
+        float ramax = 0.0f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[rt][i] = round_e4m3(h[rt][i] * s1inv);
+            rs[rt][i] = h[rt][i] - hi[rt][i] * s1;
+            ramax = fmaxf(ramax, fabsf(rs[rt][i]));
+          }
+        ramax = fmaxf(ramax, __shfl_xor(ramax, 16, 64));
+        ramax = fmaxf(ramax, __shfl_xor(ramax, 32, 64));
+        const uint32_t b2 = e4m3_block_scale_byte(ramax);
+        const float s2inv = e8m0_to_f32(254u - b2);
+        const int i = m0 + 16 * ct + r;
+        if (i < ti.cnt) {
+          const size_t pos = (size_t)ti.base + ti.row0 + i;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const size_t off = pos * f_out + w0 + 16 * rt + 4 * g;
+            *reinterpret_cast<uint32_t*>(out_hi + off) =
+                pack4_e4m3(hi[rt][0], hi[rt][1], hi[rt][2], hi[rt][3]);
+            *reinterpret_cast<uint32_t*>(out_lo + off) =
+                pack4_e4m3(round_e4m3(rs[rt][0] * s2inv), round_e4m3(rs[rt][1] * s2inv),
+                           round_e4m3(rs[rt][2] * s2inv), round_e4m3(rs[rt][3] * s2inv));
+          }
+          if (g == 0) {
+            outs_hi[pos * nbf + (w0 >> 5)] = (uint8_t)b1;
+            outs_lo[pos * nbf + (w0 >> 5)] = (uint8_t)b2;
+          }
         }
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      const uint32_t b1 = e4m3_block_scale_byte(amax);
-      const float s1 = e8m0_to_f32(b1), s1inv = e8m0_to_f32(254u - b1);
-      float hi[2][4], rs[2][4];
-      float ramax = 0.0f;
+      }
+    } else {
+      // this pair's expert output into the pair's own slot (no atomics; summed
+      // per token later; streamed past the caches, it is read once by the
+      // combine), as 24-bit floats: the wave's 64 rows of a pair are 192
+      // contiguous bytes, 64-byte aligned. Lane (r, g) holds rows
+      // 16 rt + 4 g + i of token column r; it packs each block of four rows
+      // into 12 bytes of a private LDS slice (one 192-byte row per column),
+      // then reads back and stores 16-byte pieces so that each store writes 64
+      // contiguous bytes of every column.
+      // LDS banks: a column's row starts at dword 52 r + 2 (r / 8), so the 32
+      // lanes (r, g < 2) of a half-wave's dword writes (dword 52 r + 3 g + ...
+      // modulo 32 banks) hit 32 distinct banks; without the 2-dword shift
+      // columns r and r + 8 would share banks. The shift leaves rows 8-byte
+      // aligned, so they are read back in 8-byte halves.
+      static_assert(NRT == 4, "the slot layout assumes four row tiles per wave");
+      constexpr int kStRow = 192 + 16;  // bytes per column (room for the shift)
+      __shared__ __attribute__((aligned(16))) uint32_t st_all[4][16 * kStRow / 4];
+      uint8_t* st = reinterpret_cast<uint8_t*>(st_all[wave]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (ct >= nct) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hi[rt][i] = round_e4m3(h[rt][i] * s1inv);
-          rs[rt][i] = h[rt][i] - hi[rt][i] * s1;
-          ramax = fmaxf(ramax, fabsf(rs[rt][i]));
+        for (int rt = 0; rt < NRT; ++rt) {
+          uint32_t w[3];
+          pack4_f24(acc[0][rt][ct], w);
+          uint32_t* dst =
+              reinterpret_cast<uint32_t*>(st + r * kStRow + 8 * (r >> 3) + 48 * rt + 12 * g);
+          dst[0] = w[0];
+          dst[1] = w[1];
+          dst[2] = w[2];
         }
-      ramax = fmaxf(ramax, __shfl_xor(ramax, 16, 64));
-      ramax = fmaxf(ramax, __shfl_xor(ramax, 32, 64));
-      const uint32_t b2 = e4m3_block_scale_byte(ramax);
-      const float s2inv = e8m0_to_f32(254u - b2);
-      const int i = m0 + 16 * ct + r;
-      if (i < ti.cnt) {
-        const size_t pos = (size_t)ti.base + ti.row0 + i;
+        v4u32 piece[3];  // bytes 64 q + 16 g .. + 15 of column r's 192
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const size_t off = pos * f_out + w0 + 16 * rt + 4 * g;
-          *reinterpret_cast<uint32_t*>(out_hi + off) =
-              pack4_e4m3(hi[rt][0], hi[rt][1], hi[rt][2], hi[rt][3]);
-          *reinterpret_cast<uint32_t*>(out_lo + off) =
-              pack4_e4m3(round_e4m3(rs[rt][0] * s2inv), round_e4m3(rs[rt][1] * s2inv),
-                         round_e4m3(rs[rt][2] * s2inv), round_e4m3(rs[rt][3] * s2inv));
+        for (int q = 0; q < 3; ++q) {
+          const uint8_t* src = st + r * kStRow + 8 * (r >> 3) + 64 * q + 16 * g;
+          const uint2 a = *reinterpret_cast<const uint2*>(src);
+          const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+          piece[q] = (v4u32){a.x, a.y, b.x, b.y};
         }
-        if (g == 0) {
-          outs_hi[pos * nbf + (w0 >> 5)] = (uint8_t)b1;
-          outs_lo[pos * nbf + (w0 >> 5)] = (uint8_t)b2;
+        const int i = m0 + 16 * ct + r;
+        if (i < ti.cnt) {
+          const int pair = perm[ti.base + ti.row0 + i];
+          uint8_t* o = slots + ((size_t)pair * nrows + w0) * 3 + 16 * g;
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            __builtin_nontemporal_store(piece[q], reinterpret_cast<v4u32*>(o + 64 * q));
         }
       }
     }
-  } else {
-    // this pair's expert output into the pair's own slot (no atomics; summed
-    // per token later; streamed past the caches, it is read once by the
-    // combine), as 24-bit floats: the wave's 64 rows of a pair are 192
-    // contiguous bytes, 64-byte aligned. Lane (r, g) holds rows
-    // 16 rt + 4 g + i of token column r; it packs each block of four rows
-    // into 12 bytes of a private LDS slice (one 192-byte row per column),
-    // then reads back and stores 16-byte pieces so that each store writes 64
-    // contiguous bytes of every column.
-    // LDS banks: a column's row starts at dword 52 r + 2 (r / 8), so the 32
-    // lanes (r, g < 2) of a half-wave's dword writes (dword 52 r + 3 g + ...
-    // modulo 32 banks) hit 32 distinct banks; without the 2-dword shift
-    // columns r and r + 8 would share banks. The shift leaves rows 8-byte
-    // aligned, so they are read back in 8-byte halves.
-    static_assert(NRT == 4, "the slot layout assumes four row tiles per wave");
-    constexpr int kStRow = 192 + 16;  // bytes per column (room for the shift)
-    __shared__ __attribute__((aligned(16))) uint32_t st_all[4][16 * kStRow / 4];
-    uint8_t* st = reinterpret_cast<uint8_t*>(st_all[wave]);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if (ct >= nct) continue;
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        uint32_t w[3];
-        pack4_f24(acc[0][rt][ct], w);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(st + r * kStRow + 8 * (r >> 3) + 48 * rt + 12 * g);
-        dst[0] = w[0];
-        dst[1] = w[1];
-        dst[2] = w[2];
-      }
-      v4u32 piece[3];  // bytes 64 q + 16 g .. + 15 of column r's 192
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const uint8_t* src = st + r * kStRow + 8 * (r >> 3) + 64 * q + 16 * g;
-        const uint2 a = *reinterpret_cast<const uint2*>(src);
-        const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
-        piece[q] = (v4u32){a.x, a.y, b.x, b.y};
-      }
-      const int i = m0 + 16 * ct + r;
-      if (i < ti.cnt) {
-        const int pair = perm[ti.base + ti.row0 + i];
-        uint8_t* o = slots + ((size_t)pair * nrows + w0) * 3 + 16 * g;
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          __builtin_nontemporal_store(piece[q], reinterpret_cast<v4u32*>(o + 64 * q));
-      }
-    }
-  }
   };  // k_loop: each schedule has its own accumulators, drain and epilogue
   // (the choice through a scalar register: the compiler does not know nct is
   // uniform, and a masked branch here would run both loops' registers at once)
