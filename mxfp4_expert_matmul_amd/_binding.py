@@ -130,6 +130,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# dtypes the C ABI reads (by name, so torch is imported only when used)
+_BF16 = ("bfloat16", "int16")  # x: bf16 values or their bit patterns
+_F32, _I32, _U8 = ("float32",), ("int32",), ("uint8",)
+
+
+def _dev(t, name, dtypes):
+    """Device pointer of a contiguous GPU tensor of one of `dtypes` (None
+    stays NULL). The library can check alignment only: a host pointer, a
+    strided view or another element type would be read as if it were the
+    documented layout, so they are refused here."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(dtypes)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_WEIGHT_DTYPES = {"router_w": _F32, "router_b": _F32}
+
+
+def _weights(weights: dict, host_experts: bool = False) -> "_Weights":
+    """The weight pointers: device tensors, except the six expert tensors of
+    a cache (host_experts), which are host tensors."""
+    ptrs = []
+    for n, _ in _Weights._fields_:
+        t = weights.get(n)
+        if t is None:
+            ptrs.append(None)
+        elif host_experts and n not in _WEIGHT_DTYPES:
+            ptrs.append(_host_ptr(t).value)
+        else:
+            ptrs.append(_dev(t, n, _WEIGHT_DTYPES.get(n, _U8)).value)
+    return _Weights(*ptrs)
+
+
 def _stream(stream, device):
     if stream is not None:
         return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
@@ -156,8 +195,7 @@ def k3moe_create(cfg: Config, weights: dict, device: int = 0) -> ctypes.c_void_p
     gate_s, up_q, up_s, down_q, down_s in the layout of include/k3moe.h."""
     lib = load_library()
     c = cfg._c()
-    w = _Weights(*[weights.get(n).data_ptr() if weights.get(n) is not None else None
-                   for n, _ in _Weights._fields_])
+    w = _weights(weights)
     out = ctypes.c_void_p()
     rc = lib.k3moe_create(ctypes.byref(c), ctypes.byref(w), int(device), ctypes.byref(out))
     _check(rc, "k3moe_create")
@@ -171,8 +209,10 @@ def k3moe_destroy(handle) -> None:
 
 def k3moe_layer_forward(handle, x, y, topk_idx=None, topk_gate=None, stream=None, device=None):
     T = x.shape[0]
-    rc = load_library().k3moe_layer_forward(handle, _ptr(x), T, _ptr(y), _ptr(topk_idx),
-                                            _ptr(topk_gate), _stream(stream, device or x.device))
+    rc = load_library().k3moe_layer_forward(handle, _dev(x, "x", _BF16), T, _dev(y, "y", _F32),
+                                            _dev(topk_idx, "topk_idx", _I32),
+                                            _dev(topk_gate, "topk_gate", _F32),
+                                            _stream(stream, device or x.device))
     _check(rc, "k3moe_layer_forward")
 
 
@@ -181,29 +221,34 @@ def k3moe_layer_forward_noalloc(cfg: Config, weights: dict, x, y, topk_idx=None,
     """Decode-sized forward (T <= 4) without a handle or any allocation, on
     the current device; weights as for k3moe_create."""
     c = cfg._c()
-    w = _Weights(*[weights.get(n).data_ptr() if weights.get(n) is not None else None
-                   for n, _ in _Weights._fields_])
-    rc = load_library().k3moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), _ptr(x),
-                                                    x.shape[0], _ptr(y), _ptr(topk_idx),
-                                                    _ptr(topk_gate), _stream(stream, x.device))
+    w = _weights(weights)
+    rc = load_library().k3moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w),
+                                                    _dev(x, "x", _BF16), x.shape[0],
+                                                    _dev(y, "y", _F32),
+                                                    _dev(topk_idx, "topk_idx", _I32),
+                                                    _dev(topk_gate, "topk_gate", _F32),
+                                                    _stream(stream, x.device))
     _check(rc, "k3moe_layer_forward_noalloc")
 
 
 def k3moe_route(handle, x, idx, gate, logits=None, stream=None):
-    rc = load_library().k3moe_route(handle, _ptr(x), x.shape[0], _ptr(logits), _ptr(idx),
-                                    _ptr(gate), _stream(stream, x.device))
+    rc = load_library().k3moe_route(handle, _dev(x, "x", _BF16), x.shape[0],
+                                    _dev(logits, "logits", _F32), _dev(idx, "idx", _I32),
+                                    _dev(gate, "gate", _F32), _stream(stream, x.device))
     _check(rc, "k3moe_route")
 
 
 def k3moe_group(handle, idx, counts, offsets, perm, stream=None):
-    rc = load_library().k3moe_group(handle, _ptr(idx), idx.shape[0], _ptr(counts), _ptr(offsets),
-                                    _ptr(perm), _stream(stream, idx.device))
+    rc = load_library().k3moe_group(handle, _dev(idx, "idx", _I32), idx.shape[0],
+                                    _dev(counts, "counts", _I32), _dev(offsets, "offsets", _I32),
+                                    _dev(perm, "perm", _I32), _stream(stream, idx.device))
     _check(rc, "k3moe_group")
 
 
 def k3moe_experts_forward(handle, x, idx, gate, y, stream=None):
-    rc = load_library().k3moe_experts_forward(handle, _ptr(x), x.shape[0], _ptr(idx), _ptr(gate),
-                                              _ptr(y), _stream(stream, x.device))
+    rc = load_library().k3moe_experts_forward(handle, _dev(x, "x", _BF16), x.shape[0],
+                                              _dev(idx, "idx", _I32), _dev(gate, "gate", _F32),
+                                              _dev(y, "y", _F32), _stream(stream, x.device))
     _check(rc, "k3moe_experts_forward")
 
 
@@ -212,8 +257,10 @@ def k3moe_tiled_scale_bytes(n: int, R: int, K: int) -> int:
 
 
 def k3moe_pack_mxfp4(codes, scales, n, R, K, tiled_codes, tiled_scales, stream=None):
-    rc = load_library().k3moe_pack_mxfp4(_ptr(codes), _ptr(scales), n, R, K, _ptr(tiled_codes),
-                                         _ptr(tiled_scales), _stream(stream, codes.device))
+    rc = load_library().k3moe_pack_mxfp4(_dev(codes, "codes", _U8), _dev(scales, "scales", _U8),
+                                         n, R, K, _dev(tiled_codes, "tiled_codes", _U8),
+                                         _dev(tiled_scales, "tiled_scales", _U8),
+                                         _stream(stream, codes.device))
     _check(rc, "k3moe_pack_mxfp4")
 
 
@@ -231,7 +278,8 @@ def _host_ptr(a):
 def k3moe_pack_mxfp4_from_host(codes, scales, n, R, K, tiled_codes, tiled_scales, stream=None):
     """Row-major host codes/scales (numpy or CPU tensors) -> tiled device tensors."""
     rc = load_library().k3moe_pack_mxfp4_from_host(_host_ptr(codes), _host_ptr(scales), n, R, K,
-                                                   _ptr(tiled_codes), _ptr(tiled_scales),
+                                                   _dev(tiled_codes, "tiled_codes", _U8),
+                                                   _dev(tiled_scales, "tiled_scales", _U8),
                                                    _stream(stream, tiled_codes.device))
     _check(rc, "k3moe_pack_mxfp4_from_host")
 
@@ -323,8 +371,7 @@ class CachedLayer:
         self._weights = host_weights
         self.device_plan = bool(device_plan)
         c = cfg._c()
-        w = _Weights(*[host_weights.get(n).data_ptr() if host_weights.get(n) is not None else None
-                       for n, _ in _Weights._fields_])
+        w = _weights(host_weights, host_experts=True)
         out = ctypes.c_void_p()
         flags = K3MOE_CACHE_DEVICE_PLAN if device_plan else 0
         _check(lib.k3moe_cache_create_ex(ctypes.byref(c), ctypes.byref(w), int(n_slots),
@@ -340,8 +387,8 @@ class CachedLayer:
         y = torch.empty((T, self.cfg.d_model), dtype=torch.float32, device=dev)
         idx = torch.empty((T, self.cfg.top_k), dtype=torch.int32, device=dev)
         gate = torch.empty((T, self.cfg.top_k), dtype=torch.float32, device=dev)
-        _check(load_library().k3moe_cache_forward(self.handle, _ptr(x), T, _ptr(y), _ptr(idx),
-                                                  _ptr(gate), _stream(stream, dev)),
+        _check(load_library().k3moe_cache_forward(self.handle, _dev(x, "x", _BF16), T, _ptr(y),
+                                                  _ptr(idx), _ptr(gate), _stream(stream, dev)),
                "k3moe_cache_forward")
         return y, idx, gate
 
@@ -360,8 +407,9 @@ class CachedLayer:
         contiguous int32 tensor on the GPU (read when the plan runs), on
         `stream` (torch stream or None for the current one)."""
         n = experts.numel()
+        ptr = _dev(experts, "experts", _I32)
         _check(load_library().k3moe_cache_prefetch_device(
-            self.handle, _ptr(experts) if n else None, n, _stream(stream, experts.device)),
+            self.handle, ptr if n else None, n, _stream(stream, experts.device)),
             "k3moe_cache_prefetch_device")
 
     def device_counters(self) -> dict:

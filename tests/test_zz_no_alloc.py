@@ -135,10 +135,12 @@ def test_noalloc_refusals(k3):
     ]
     for cfg, T, want in cases:
         with pytest.raises(k3.K3MoEError) as ei:
-            k3.k3moe_layer_forward_noalloc(cfg, dummy, x[:T, :cfg.d_model], y[:T, :cfg.d_model])
+            k3.k3moe_layer_forward_noalloc(cfg, dummy, x[:T, :cfg.d_model].contiguous(),
+                                           y[:T, :cfg.d_model].contiguous())
         assert ei.value.status == want, (cfg, T)
     idx = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
     with pytest.raises(k3.K3MoEError) as ei:
-        k3.k3moe_layer_forward_noalloc(k3.Config(2048, 64, 8, 1024, 4), dummy, x[:1, :2048],
-                                       y[:1, :2048], topk_idx=idx)
+        k3.k3moe_layer_forward_noalloc(k3.Config(2048, 64, 8, 1024, 4), dummy,
+                                       x[:1, :2048].contiguous(), y[:1, :2048].contiguous(),
+                                       topk_idx=idx)
     assert ei.value.status == k3.K3MOE_EINVAL
