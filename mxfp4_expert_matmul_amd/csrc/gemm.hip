@@ -474,8 +474,14 @@ __global__ __launch_bounds__(kThreads, 2) void mx_gemm_kernel(
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         piece(ct);  // loads issued ahead of this column tile (if any)
+        // The next column tile's B reads go out whether or not it holds
+        // tokens (its rows are inside the stage; the values of an empty one
+        // go unused). Behind a branch on that tile's tokens, the compiler could
+        // not tell how many LDS reads follow this tile's and waited for all
+        // of them before this tile's MFMAs (measured: gate/up 0.6%, down
+        // 0.8% faster).
+        if (ct + 1 < NCT) b_load(L, ct + 1, b[(ct + 1) & 1]);
         if (ct < nct) {
-          if (ct + 1 < nct) b_load(L, ct + 1, b[(ct + 1) & 1]);
           const BFrag& cb = b[ct & 1];
 #pragma unroll
           for (int m = 0; m < NM; ++m)
