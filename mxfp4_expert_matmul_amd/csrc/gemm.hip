@@ -732,14 +732,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
   if (i >= (size_t)T * d4) return;
   const int t = (int)(i / d4), c = (int)(i % d4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // every slot is read (a dropped pair's slot is allocated but unwritten and
-  // its values are replaced by zero, not multiplied), so the loads of several
-  // slots are in flight together
-#pragma unroll 4
+  // every slot and gate is read (a dropped pair's slot is allocated but
+  // unwritten and its values are replaced by zero, not multiplied), so the
+  // loop has no branch and the loads of all its slots are in flight together
+  // (a gate read only for a kept pair made one branch per slot, and the
+  // compiler waited for the loads at each: 8% slower)
+#pragma unroll 16
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
+    const float g = gate[(size_t)t * k + j];
     const bool on = e >= 0 && e < E;
-    const float gw = on ? gate[(size_t)t * k + j] : 0.0f;
+    const float gw = on ? g : 0.0f;
     const v3u32 w3 = __builtin_nontemporal_load(
         reinterpret_cast<const v3u32*>(slots + (((size_t)t * k + j) * d + 4 * (size_t)c) * 3));
     const uint32_t w[3] = {w3[0], w3[1], w3[2]};
