@@ -27,29 +27,34 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
   const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * d);
   constexpr int kMaxPer = 8;  // float4 per thread for d <= 8192
   const int n4 = d >> 2;
+  // every load is issued, with its index clamped into the row, before any
+  // is used (a load behind a branch made the compiler wait for each x load
+  // in turn); an out-of-row piece's sum is then dropped by a select
   float4 w[kMaxPer];
+  uint2 xv[kMaxPer][TMAX];
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j) {
-    const int i = tid + 256 * j;
-    if (i < n4) w[j] = row[i];
+    const int i = min(tid + 256 * j, n4 - 1);
+    w[j] = row[i];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+      xv[j][t] = *reinterpret_cast<const uint2*>(x + (size_t)min(t, T - 1) * d + 4 * i);
   }
   float acc[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) acc[t] = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j) {
-    const int i = tid + 256 * j;
-    if (i < n4) {
+    const bool in = tid + 256 * j < n4;
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-          uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + 4 * i);
-          acc[t] = fmaf(bf16_bits_to_f32(xv.x & 0xffffu), w[j].x, acc[t]);
-          acc[t] = fmaf(bf16_bits_to_f32(xv.x >> 16), w[j].y, acc[t]);
-          acc[t] = fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w[j].z, acc[t]);
-          acc[t] = fmaf(bf16_bits_to_f32(xv.y >> 16), w[j].w, acc[t]);
-        }
-      }
+    for (int t = 0; t < TMAX; ++t) {
+      const uint2 v = xv[j][t];
+      float a = acc[t];
+      a = fmaf(bf16_bits_to_f32(v.x & 0xffffu), w[j].x, a);
+      a = fmaf(bf16_bits_to_f32(v.x >> 16), w[j].y, a);
+      a = fmaf(bf16_bits_to_f32(v.y & 0xffffu), w[j].z, a);
+      a = fmaf(bf16_bits_to_f32(v.y >> 16), w[j].w, a);
+      acc[t] = in ? a : acc[t];  // the same sum, in the same order, as before
     }
   }
 #pragma unroll
